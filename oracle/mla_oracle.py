@@ -1,0 +1,276 @@
+"""Explicit Multi-head Latent Attention in float64 on the CPU: the oracle.
+
+TEST INFRASTRUCTURE, NOT PART OF THE LIBRARY.  Only the tests, the smoke check
+and the CPU-baseline leg of the benchmark may import this module.  It shares no
+code with the HIP path and imports nothing from the library package.
+
+What it follows.  The notes page "【论文解读】DeepSeek-V3" (wkq9411.github.io),
+section 一(一) "多头潜在注意力MLA":
+  * 1 "回顾多头注意力MHA": per-head softmax attention, Softmax_j over j = 1..t,
+    heads are consecutive d_h-row blocks of the projections;
+  * 2 "低秩KV联合压缩": c^KV = W^DKV h, k^C = W^UK c^KV, v^C = W^UV c^KV,
+    c^Q = W^DQ h, q^C = W^UQ c^Q;
+  * 【思考】 on absorption: per-head blocks W_i^UK, W_i^UV in R^{d_h x d_c};
+    q^C_i . k^C_{j,i} = (W_i^UK^T q^C_i) . c_j and o_i = W_i^UV sum_j a_j c_j;
+  * 3 "解耦RoPE": q^R = RoPE(W^QR c^Q) per head, k^R = RoPE(W^KR h) shared by
+    all heads, q_i = [q^C_i; q^R_i], k_i = [k^C_i; k^R], scale 1/sqrt(d_h+d_h^R);
+  * the ten-step "完整计算过程" list, steps (1)-(10);
+  * section 二(二)1: "an additional RMSNorm after the compressed latent vectors".
+
+The result has a plain definition (steps (1)-(10)), so the oracle is that
+definition written out: it materialises every head's k and v and applies the
+max-subtracted softmax, all in float64.  The absorbed form (used only by the
+pins, to show the two forms agree) is a separate function.
+
+Readings where the pages leave a step open (each listed with its reason in the
+design notes of the repository):
+  * RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, applied to both c^KV and c^Q;
+    k^R is not normalised (it is taken from h, not from a latent).
+  * RoPE: rotation of adjacent pairs (x_2p, x_2p+1) by the 2x2 block
+    [[cos, -sin], [sin, cos]] of section 一(一)3, angle pos * theta_p with
+    theta_p = base^(-2p/d_rope) (the RoPE frequency formula quoted on the
+    hnwysp.cn digest, section 4.3), base 10000, positions counted from 0.
+  * Output stops at o = [o_1; ...; o_{n_h}]; W^O is not applied.
+  * Decode: the step's s_q new tokens are already cached; query s of a
+    sequence with kv_len cached rows sits at position kv_len - s_q + s and
+    attends to rows j <= that position.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# Building blocks
+# ---------------------------------------------------------------------------
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (section 二(二)1: RMSNorm after the latents)."""
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(g)
+
+
+def rope_frequencies(d_rope: int, base: float) -> np.ndarray:
+    """theta_p = base^(-2p/d_rope), p = 0 .. d_rope/2 - 1."""
+    p = np.arange(d_rope // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * p / d_rope)
+
+
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rotate each adjacent pair of the last axis by pos * theta_p.
+
+    Section 一(一)3 gives R_m as a block-diagonal matrix of 2x2 rotations
+    [[cos m.theta, -sin m.theta], [sin m.theta, cos m.theta]].  ``x`` is
+    [..., d_rope]; ``pos`` broadcasts against x's leading axes.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    theta = rope_frequencies(d, base)
+    ang = _f64(pos)[..., None] * theta            # [..., d/2]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = c * x0 - s * x1
+    out[..., 1::2] = s * x0 + c * x1
+    return out
+
+
+def split_heads(x, n_heads: int) -> np.ndarray:
+    """[..., n_heads * w] -> [..., n_heads, w]: head i owns block i (section 一(一)1)."""
+    x = _f64(x)
+    return x.reshape(*x.shape[:-1], n_heads, x.shape[-1] // n_heads)
+
+
+# ---------------------------------------------------------------------------
+# Projections (steps (1)-(3), (5), (7))
+# ---------------------------------------------------------------------------
+def query_path(h, w_dq, g_q, w_uq, w_qr, pos, n_heads: int, eps: float, base: float):
+    """Steps (1)-(3): c^Q = RMSNorm(W^DQ h); q^C = W^UQ c^Q; q^R = RoPE(W^QR c^Q).
+
+    h: [T, d]; pos: [T].  Returns q^C [T, H, d_h] and q^R [T, H, d_rope].
+    """
+    h = _f64(h)
+    c_q = rms_norm(h @ _f64(w_dq).T, g_q, eps)
+    q_c = split_heads(c_q @ _f64(w_uq).T, n_heads)
+    q_r_raw = split_heads(c_q @ _f64(w_qr).T, n_heads)
+    q_r = rope(q_r_raw, _f64(pos)[:, None], base)
+    return q_c, q_r
+
+
+def latent_rows(h, w_dkv, g_kv, w_kr, pos, eps: float, base: float):
+    """Steps (5) and (7): c^KV = RMSNorm(W^DKV h) and k^R = RoPE(W^KR h).
+
+    These two vectors are all that is cached per token (section 一(一)3, end of
+    the decoupled-RoPE equations).  Returns (c [T, d_c], k_r [T, d_rope]).
+    """
+    h = _f64(h)
+    c = rms_norm(h @ _f64(w_dkv).T, g_kv, eps)
+    k_r = rope(h @ _f64(w_kr).T, pos, base)
+    return c, k_r
+
+
+def cache_row(c_raw, k_raw, g_kv, pos, eps: float, base: float) -> np.ndarray:
+    """One cached row from the raw projections: [RMSNorm(c_raw) ; RoPE(k_raw, pos)]."""
+    return np.concatenate([rms_norm(c_raw, g_kv, eps), rope(k_raw, pos, base)], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Attention (steps (6), (8), (9), (10)), explicit form
+# ---------------------------------------------------------------------------
+def explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, scale: float,
+                       heads=None, return_weights: bool = False):
+    """Explicit MLA attention of some queries over one sequence's cached rows.
+
+    q_c [T, H, d_h], q_r [T, H, d_rope] (already rotated), c [N, d_c],
+    k_r [N, d_rope] (already rotated), w_uk / w_uv [H*d_h, d_c], q_pos [T]:
+    query t attends to rows j <= q_pos[t].  For every head i it materialises
+    k^C_{j,i} = W_i^UK c_j, k_{j,i} = [k^C_{j,i}; k^R_j], v_{j,i} = W_i^UV c_j
+    and computes o_{t,i} = sum_j Softmax_j(q_{t,i} . k_{j,i} * scale) v_{j,i}.
+    Returns o [T, len(heads), d_h] (and the weights [T, len(heads), N]).
+    """
+    q_c, q_r, c, k_r = _f64(q_c), _f64(q_r), _f64(c), _f64(k_r)
+    T, H, dh = q_c.shape
+    N = c.shape[0]
+    heads = list(range(H)) if heads is None else list(heads)
+    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    visible = np.arange(N)[None, :] <= q_pos[:, None]          # [T, N]
+    out = np.zeros((T, len(heads), dh), F64)
+    wts = np.zeros((T, len(heads), N), F64) if return_weights else None
+    for n, i in enumerate(heads):
+        wk = w_uk[i * dh:(i + 1) * dh]                         # W_i^UK [d_h, d_c]
+        wv = w_uv[i * dh:(i + 1) * dh]                         # W_i^UV [d_h, d_c]
+        k_c = c @ wk.T                                          # [N, d_h]
+        v = c @ wv.T                                            # [N, d_h]
+        k = np.concatenate([k_c, k_r], axis=1)                  # [N, d_h + d_rope]
+        q = np.concatenate([q_c[:, i], q_r[:, i]], axis=1)      # [T, d_h + d_rope]
+        s = (q @ k.T) * scale
+        s = np.where(visible, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=1, keepdims=True)
+        out[:, n] = a @ v
+        if return_weights:
+            wts[:, n] = a
+    return (out, wts) if return_weights else out
+
+
+def absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, scale: float, heads=None):
+    """The same attention with W^UK folded into the query and W^UV after the sum.
+
+    q_lat_{t,i} = W_i^UK^T q^C_{t,i}; score = q_lat . c_j + q^R_{t,i} . k^R_j;
+    o_{t,i} = W_i^UV sum_j a_j c_j  (【思考】 on absorption, and the score split
+    into a latent term and a RoPE term in section 一(一)3).
+    """
+    q_c, q_r, c, k_r = _f64(q_c), _f64(q_r), _f64(c), _f64(k_r)
+    T, H, dh = q_c.shape
+    N = c.shape[0]
+    heads = list(range(H)) if heads is None else list(heads)
+    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
+    visible = np.arange(N)[None, :] <= np.asarray(q_pos, np.int64)[:, None]
+    out = np.zeros((T, len(heads), dh), F64)
+    for n, i in enumerate(heads):
+        q_lat = q_c[:, i] @ w_uk[i * dh:(i + 1) * dh]          # [T, d_c]
+        s = (q_lat @ c.T + q_r[:, i] @ k_r.T) * scale
+        s = np.where(visible, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=1, keepdims=True)
+        out[:, n] = (a @ c) @ w_uv[i * dh:(i + 1) * dh].T
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Split-context partials and their merge
+# ---------------------------------------------------------------------------
+def latent_partial(q_lat, q_r, c, k_r, scale: float, lo: int, hi: int):
+    """Softmax partial of one query head over rows [lo, hi) of its visible range.
+
+    Returns (m, l, acc): m = max score, l = sum_j e^{s_j - m},
+    acc = sum_j e^{s_j - m} c_j.  An empty range gives (-inf, 0, 0).
+    """
+    q_lat, q_r, c, k_r = _f64(q_lat), _f64(q_r), _f64(c), _f64(k_r)
+    if hi <= lo:
+        return -np.inf, 0.0, np.zeros(c.shape[1], F64)
+    s = (c[lo:hi] @ q_lat + k_r[lo:hi] @ q_r) * scale
+    m = s.max()
+    e = np.exp(s - m)
+    return m, e.sum(), e @ c[lo:hi]
+
+
+def merge_partials(ms, ls, accs) -> np.ndarray:
+    """Combine split partials: m* = max m_k; result = sum e^{m_k-m*} acc_k / sum e^{m_k-m*} l_k.
+
+    This is the identity softmax(x) over a union of disjoint ranges satisfies;
+    the pages are silent on splitting, so the merge is written from it.
+    """
+    ms = _f64(ms)
+    ls = _f64(ls)
+    accs = _f64(accs)
+    m_star = ms.max()
+    w = np.exp(ms - m_star)
+    return (w[:, None] * accs).sum(axis=0) / (w * ls).sum()
+
+
+# ---------------------------------------------------------------------------
+# Whole operations, as the library exposes them
+# ---------------------------------------------------------------------------
+def decode(rows_per_seq, kv_lens, s_q: int, q_nope, q_pe, w_uk, w_uv, d_c: int, scale: float,
+           seqs=None, heads=None) -> np.ndarray:
+    """One decode step over cached rows ([c ; k^R] per token, position order).
+
+    rows_per_seq[b] is [kv_len_b, d_c + d_rope]; q_nope [B, s_q, H, d_h];
+    q_pe [B, s_q, H, d_rope] (rotated).  Returns o [len(seqs), s_q, len(heads), d_h].
+    """
+    seqs = range(len(kv_lens)) if seqs is None else seqs
+    outs = []
+    for b in seqs:
+        rows = _f64(rows_per_seq[b])
+        kv = int(kv_lens[b])
+        q_pos = kv - s_q + np.arange(s_q)
+        outs.append(explicit_attention(q_nope[b], q_pe[b], rows[:kv, :d_c], rows[:kv, d_c:],
+                                       w_uk, w_uv, q_pos, scale, heads=heads))
+    return np.stack(outs)
+
+
+def prefill(h, w, n_heads: int, eps: float, base: float, scale: float, start_pos: int = 0,
+            past_rows=None, tokens=None, heads=None):
+    """Steps (1)-(10) for one sequence: h [L, d] holds tokens start_pos .. start_pos+L-1.
+
+    ``past_rows`` [start_pos, d_c + d_rope] are the rows already cached for
+    earlier positions.  Returns (o [len(tokens), len(heads), d_h], new_rows
+    [L, d_c + d_rope]).  ``tokens`` selects which new tokens' outputs to compute.
+    """
+    h = _f64(h)
+    L = h.shape[0]
+    pos = start_pos + np.arange(L)
+    d_c = np.asarray(w["w_dkv"]).shape[0]
+    c, k_r = latent_rows(h, w["w_dkv"], w["g_kv"], w["w_kr"], pos, eps, base)
+    new_rows = np.concatenate([c, k_r], axis=1)
+    rows = new_rows if past_rows is None or start_pos == 0 else np.concatenate([_f64(past_rows), new_rows])
+    tokens = np.arange(L) if tokens is None else np.asarray(tokens)
+    q_c, q_r = query_path(h[tokens], w["w_dq"], w["g_q"], w["w_uq"], w["w_qr"], pos[tokens],
+                          n_heads, eps, base)
+    o = explicit_attention(q_c, q_r, rows[:, :d_c], rows[:, d_c:], w["w_uk"], w["w_uv"],
+                           pos[tokens], scale, heads=heads)
+    return o, new_rows
+
+
+# ---------------------------------------------------------------------------
+# Paged layout
+# ---------------------------------------------------------------------------
+def paged_slot(block_table, b: int, pos: int, page_size: int):
+    """Where token ``pos`` of sequence ``b`` lives: (page id, slot in page)."""
+    return int(block_table[b][pos // page_size]), pos % page_size
+
+
+def paged_gather(pool, block_table, b: int, n: int, page_size: int) -> np.ndarray:
+    """Rows 0..n-1 of sequence b, read through the block table."""
+    return np.stack([pool[paged_slot(block_table, b, p, page_size)] for p in range(n)]) if n else \
+        np.zeros((0,) + pool.shape[2:], pool.dtype)

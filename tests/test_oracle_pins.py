@@ -1,0 +1,374 @@
+"""Pins for the float64 oracle: checks against things other than the oracle itself.
+
+Each test names what fixes the expected value: a closed form, an identity the
+notes page derives, a library routine the method reduces to in a special case,
+a brute-force loop written from the definitions, or a value the pages print
+(``tests/golden``).  A plausible slip in the oracle -- a dropped RoPE term, a
+wrong sign, a transposed per-head block, an off-by-one causal mask, a wrong
+scale -- fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import mla_oracle as om
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "v3_mla_constants.json")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _rand_setup(seed, H=3, dh=4, dr=2, dc=6, dcq=5, d=7, L=6):
+    r = np.random.default_rng(seed)
+    w = {
+        "w_dq": r.standard_normal((dcq, d)), "g_q": r.uniform(0.5, 1.5, dcq),
+        "w_uq": r.standard_normal((H * dh, dcq)), "w_qr": r.standard_normal((H * dr, dcq)),
+        "w_dkv": r.standard_normal((dc, d)), "g_kv": r.uniform(0.5, 1.5, dc),
+        "w_kr": r.standard_normal((dr, d)),
+        "w_uk": r.standard_normal((H * dh, dc)), "w_uv": r.standard_normal((H * dh, dc)),
+    }
+    h = r.standard_normal((L, d))
+    return w, h
+
+
+# ---------------------------------------------------------------------------
+# Brute force (P4): scalar loops written straight from steps (1)-(10) of the
+# notes page, no matrix library.  Tiny shapes only.
+# ---------------------------------------------------------------------------
+def _bf_matvec(W, x):
+    return [sum(W[r][k] * x[k] for k in range(len(x))) for r in range(len(W))]
+
+
+def _bf_rms(x, g, eps):
+    ms = sum(v * v for v in x) / len(x)
+    return [x[k] / math.sqrt(ms + eps) * g[k] for k in range(len(x))]
+
+
+def _bf_rope(x, pos, base):
+    d = len(x)
+    y = list(x)
+    for p in range(d // 2):
+        th = pos * base ** (-2.0 * p / d)
+        c, s = math.cos(th), math.sin(th)
+        # R = [[c, -s], [s, c]] applied to the column (x_2p, x_2p+1)
+        y[2 * p] = c * x[2 * p] - s * x[2 * p + 1]
+        y[2 * p + 1] = s * x[2 * p] + c * x[2 * p + 1]
+    return y
+
+
+def _bf_prefill(h, w, H, eps, base):
+    W = {k: np.asarray(v).tolist() for k, v in w.items()}
+    L = len(h)
+    dh = len(W["w_uq"]) // H
+    dr = len(W["w_kr"])
+    hs = np.asarray(h).tolist()
+    q, k, v = [], [], []
+    for t in range(L):
+        cq = _bf_rms(_bf_matvec(W["w_dq"], hs[t]), W["g_q"], eps)            # (1)
+        qc = _bf_matvec(W["w_uq"], cq)                                       # (2)
+        qr_all = _bf_matvec(W["w_qr"], cq)                                   # (3)
+        ckv = _bf_rms(_bf_matvec(W["w_dkv"], hs[t]), W["g_kv"], eps)         # (5)
+        kc = _bf_matvec(W["w_uk"], ckv)                                      # (6)
+        kr = _bf_rope(_bf_matvec(W["w_kr"], hs[t]), t, base)                 # (7)
+        vc = _bf_matvec(W["w_uv"], ckv)                                      # (9)
+        q.append([qc[i * dh:(i + 1) * dh] + _bf_rope(qr_all[i * dr:(i + 1) * dr], t, base)
+                  for i in range(H)])                                        # (4)
+        k.append([kc[i * dh:(i + 1) * dh] + kr for i in range(H)])           # (8)
+        v.append([vc[i * dh:(i + 1) * dh] for i in range(H)])
+    scale = 1.0 / math.sqrt(dh + dr)
+    out = np.zeros((L, H, dh))
+    for t in range(L):                                                       # (10)
+        for i in range(H):
+            sc = [sum(a * b for a, b in zip(q[t][i], k[j][i])) * scale for j in range(t + 1)]
+            m = max(sc)
+            e = [math.exp(s - m) for s in sc]
+            tot = sum(e)
+            for j in range(t + 1):
+                for a in range(dh):
+                    out[t, i, a] += e[j] / tot * v[j][i][a]
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_p4_bruteforce_matches_oracle(seed):
+    w, h = _rand_setup(seed)
+    H, eps, base = 3, 1e-6, 10000.0
+    ref = _bf_prefill(h, w, H, eps, base)
+    o, _ = om.prefill(h, w, H, eps, base, scale=1.0 / math.sqrt(4 + 2))
+    assert _rel(o, ref) <= 1e-13
+
+
+def test_p4_bruteforce_tiny_base_large_angles():
+    # a small RoPE base makes every pair rotate visibly, so a pairing slip shows
+    w, h = _rand_setup(7, L=5)
+    ref = _bf_prefill(h, w, 3, 1e-6, 3.0)
+    o, _ = om.prefill(h, w, 3, 1e-6, 3.0, scale=1.0 / math.sqrt(6))
+    assert _rel(o, ref) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# P1: absorbed form == explicit form (【思考】 on absorption)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p1_absorbed_equals_explicit(seed):
+    r = np.random.default_rng(100 + seed)
+    H, dh, dr, dc, N, T = 4, 8, 4, 16, 23, 5
+    q_c = r.standard_normal((T, H, dh))
+    q_r = r.standard_normal((T, H, dr))
+    c = r.standard_normal((N, dc))
+    k_r = r.standard_normal((N, dr))
+    w_uk = r.standard_normal((H * dh, dc)) / 4
+    w_uv = r.standard_normal((H * dh, dc)) / 4
+    q_pos = np.array([0, 5, 11, 17, 22])
+    a = om.explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.3)
+    b = om.absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.3)
+    assert _rel(b, a) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P2: with d_c = n_h d_h and identity up-projections MLA is textbook causal MHA,
+# checked against torch's scaled_dot_product_attention in float64 on the CPU.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("zero_rope", [False, True])
+def test_p2_reduces_to_mha(zero_rope):
+    r = np.random.default_rng(5)
+    H, dh, dr, L = 3, 4, 2, 9
+    dc = H * dh
+    q_c = r.standard_normal((L, H, dh))
+    q_r = np.zeros((L, H, dr)) if zero_rope else r.standard_normal((L, H, dr))
+    c = r.standard_normal((L, dc))
+    k_r = np.zeros((L, dr)) if zero_rope else r.standard_normal((L, dr))
+    eye = np.eye(dc)
+    scale = 1.0 / math.sqrt(dh + dr)
+    o = om.explicit_attention(q_c, q_r, c, k_r, eye, eye, np.arange(L), scale)
+    # MHA: head i's key is [c_j block i ; k^R_j], value is c_j block i
+    q = torch.from_numpy(np.concatenate([q_c, q_r], axis=2)).permute(1, 0, 2)          # [H, L, E]
+    kb = np.stack([np.concatenate([c[:, i * dh:(i + 1) * dh], k_r], axis=1) for i in range(H)])
+    vb = np.stack([c[:, i * dh:(i + 1) * dh] for i in range(H)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, torch.from_numpy(kb), torch.from_numpy(vb), is_causal=True, scale=scale)
+    assert _rel(o, ref.permute(1, 0, 2).numpy()) <= 1e-12
+
+
+def test_p2_permuted_up_projection_matches_mha():
+    # a non-symmetric (permutation) W^UK catches a transposed per-head block
+    r = np.random.default_rng(6)
+    H, dh, dr, L = 2, 3, 2, 7
+    dc = H * dh
+    perm = r.permutation(dc)
+    P = np.eye(dc)[perm]
+    q_c = r.standard_normal((L, H, dh))
+    q_r = r.standard_normal((L, H, dr))
+    c = r.standard_normal((L, dc))
+    k_r = r.standard_normal((L, dr))
+    scale = 1.0 / math.sqrt(dh + dr)
+    o = om.explicit_attention(q_c, q_r, c, k_r, P, np.eye(dc), np.arange(L), scale)
+    pc = c[:, perm]                       # (P c_j) = c_j permuted
+    q = torch.from_numpy(np.concatenate([q_c, q_r], axis=2)).permute(1, 0, 2)
+    kb = np.stack([np.concatenate([pc[:, i * dh:(i + 1) * dh], k_r], axis=1) for i in range(H)])
+    vb = np.stack([c[:, i * dh:(i + 1) * dh] for i in range(H)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, torch.from_numpy(kb), torch.from_numpy(vb), is_causal=True, scale=scale)
+    assert _rel(o, ref.permute(1, 0, 2).numpy()) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P3: softmax weights are a distribution over the visible rows
+# ---------------------------------------------------------------------------
+def test_p3_weights_are_causal_distributions():
+    r = np.random.default_rng(9)
+    H, dh, dr, dc, N = 3, 4, 2, 8, 12
+    q_pos = np.array([0, 3, 11])
+    _, a = om.explicit_attention(r.standard_normal((3, H, dh)), r.standard_normal((3, H, dr)),
+                                 r.standard_normal((N, dc)), r.standard_normal((N, dr)),
+                                 r.standard_normal((H * dh, dc)), r.standard_normal((H * dh, dc)),
+                                 q_pos, 0.5, return_weights=True)
+    assert np.all(a >= 0)
+    assert np.max(np.abs(a.sum(axis=2) - 1.0)) <= 1e-12
+    for t, p in enumerate(q_pos):
+        assert np.all(a[t, :, p + 1:] == 0.0)
+        assert np.all(a[t, :, :p + 1] > 0.0)
+
+
+# ---------------------------------------------------------------------------
+# P5: RoPE
+# ---------------------------------------------------------------------------
+def test_p5_rope_matches_complex_rotation():
+    r = np.random.default_rng(11)
+    x = r.standard_normal((5, 8))
+    pos = np.array([0, 1, 7, 100, 131072])
+    y = om.rope(x, pos, 10000.0)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * pos[:, None] * 10000.0 ** (-np.arange(4) * 2 / 8))
+    assert np.max(np.abs(y[:, 0::2] - z.real)) <= 1e-12
+    assert np.max(np.abs(y[:, 1::2] - z.imag)) <= 1e-12
+
+
+def test_p5_rope_block_from_page():
+    g = json.load(open(GOLDEN))["rope_block"]
+    assert g["rotate_unit_x"] == "cos_sin"
+    y = om.rope(np.array([1.0, 0.0]), 3, 10000.0)        # theta_0 = 1, angle 3
+    assert np.allclose(y, [math.cos(3.0), math.sin(3.0)], atol=1e-15)
+
+
+def test_p5_rope_identity_at_zero_and_norm_preserving():
+    r = np.random.default_rng(12)
+    x = r.standard_normal((4, 64))
+    assert np.array_equal(om.rope(x, np.zeros(4), 10000.0), x)
+    y = om.rope(x, np.array([1, 50, 4097, 32769]), 10000.0)
+    for p in range(32):
+        assert np.allclose(np.hypot(y[:, 2 * p], y[:, 2 * p + 1]), np.hypot(x[:, 2 * p], x[:, 2 * p + 1]),
+                           rtol=1e-13)
+
+
+def test_p5_scores_depend_only_on_relative_position():
+    r = np.random.default_rng(13)
+    H, dh, dr, dc, N = 2, 4, 6, 8, 10
+    q_c = r.standard_normal((3, H, dh))
+    q_raw = r.standard_normal((3, H, dr))
+    c = r.standard_normal((N, dc))
+    k_raw = r.standard_normal((N, dr))
+    w_uk = r.standard_normal((H * dh, dc))
+    w_uv = r.standard_normal((H * dh, dc))
+    q_pos = np.array([2, 6, 9])
+    outs = []
+    for shift in [0, 17, 4093]:
+        q_r = om.rope(q_raw, (q_pos + shift)[:, None], 10000.0)
+        k_r = om.rope(k_raw, np.arange(N) + shift, 10000.0)
+        outs.append(om.explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.4))
+    assert _rel(outs[1], outs[0]) <= 1e-10 and _rel(outs[2], outs[0]) <= 1e-10
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+def test_rmsnorm_closed_forms():
+    g = np.linspace(0.5, 1.5, 16)
+    # a constant vector c*1 normalises to g * c / sqrt(c^2 + eps)
+    y = om.rms_norm(np.full(16, 3.0), g, 1e-6)
+    assert np.allclose(y, g * 3.0 / math.sqrt(9.0 + 1e-6), rtol=1e-15)
+    r = np.random.default_rng(14)
+    x = r.standard_normal((3, 16))
+    y0 = om.rms_norm(x, np.ones(16), 0.0)
+    assert np.allclose(np.mean(y0 * y0, axis=1), 1.0, rtol=1e-14)
+    assert np.allclose(om.rms_norm(7.5 * x, np.ones(16), 0.0), y0, rtol=1e-14)
+    assert np.allclose(om.rms_norm(x, g, 0.0), y0 * g, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# P6: closed forms of attention
+# ---------------------------------------------------------------------------
+def test_p6_first_token_and_identical_keys():
+    r = np.random.default_rng(15)
+    H, dh, dr, dc, N = 3, 4, 2, 8, 9
+    q_c = r.standard_normal((2, H, dh))
+    q_r = r.standard_normal((2, H, dr))
+    w_uk = r.standard_normal((H * dh, dc))
+    w_uv = r.standard_normal((H * dh, dc))
+    c = r.standard_normal((N, dc))
+    k_r = r.standard_normal((N, dr))
+    o = om.explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, np.array([0, 0]), 0.7)
+    for i in range(H):
+        assert np.allclose(o[:, i], (w_uv[i * dh:(i + 1) * dh] @ c[0])[None], rtol=1e-14)
+    c_same = np.repeat(c[:1], N, axis=0)
+    k_same = np.repeat(k_r[:1], N, axis=0)
+    o = om.explicit_attention(q_c, q_r, c_same, k_same, w_uk, w_uv, np.array([N - 1, 4]), 0.7)
+    for i in range(H):
+        assert np.allclose(o[:, i], (w_uv[i * dh:(i + 1) * dh] @ c[0])[None], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P7: merging split partials equals the unsplit softmax
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cuts", [[0, 40], [0, 1, 40], [0, 13, 13, 27, 40], [0, 39, 40]])
+def test_p7_merge_identity(cuts):
+    r = np.random.default_rng(16)
+    dc, dr, N = 12, 4, 40
+    c = r.standard_normal((N, dc))
+    k_r = r.standard_normal((N, dr))
+    q_lat = r.standard_normal(dc) * 2
+    q_r = r.standard_normal(dr)
+    parts = [om.latent_partial(q_lat, q_r, c, k_r, 0.5, lo, hi) for lo, hi in zip(cuts[:-1], cuts[1:])]
+    merged = om.merge_partials([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
+    s = (c @ q_lat + k_r @ q_r) * 0.5
+    a = np.exp(s - s.max())
+    a /= a.sum()
+    assert _rel(merged, a @ c) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P8: layout constants printed on the pages
+# ---------------------------------------------------------------------------
+def test_p8_layout_constants():
+    g = json.load(open(GOLDEN))
+    hp = g["v3_hyperparameters"]
+    s = mi.V3
+    assert (s.n_heads, s.d_head, s.d_c, s.d_cq, s.d_rope, s.d_model) == \
+        (hp["n_heads"], hp["d_head"], hp["d_c"], hp["d_cq"], hp["d_rope"], hp["d_model"])
+    assert s.d_c == g["v2_ratios"]["d_c_over_d_head"] * s.d_head
+    assert s.d_rope == g["v2_ratios"]["d_rope_over_d_head"] * s.d_head
+    assert s.row == g["cache_elements_per_token_per_layer"]["mla"]
+    assert 2 * s.n_heads * s.d_head == g["cache_elements_per_token_per_layer"]["mha"]
+    assert s.d_head + s.d_rope == g["softmax_scale_denominator_squared"]["value"]
+    lc = g["long_context_latent_bytes_per_sequence"]
+    assert lc["tokens"] * s.row * 2 == lc["bytes"]
+    assert round(lc["bytes"] / 1e6) == 151
+
+
+# ---------------------------------------------------------------------------
+# P10 (oracle side): paged placement is a bijection onto the pool
+# ---------------------------------------------------------------------------
+def test_p10_paged_slots_are_a_bijection():
+    kv = np.array([1, 64, 65, 130, 7])
+    bt, npages = mi.block_table(3, kv, 64, shuffle=True)
+    seen = set()
+    for b, n in enumerate(kv):
+        for p in range(n):
+            slot = om.paged_slot(bt, b, p, 64)
+            assert 0 <= slot[0] < npages and 0 <= slot[1] < 64
+            assert slot not in seen
+            seen.add(slot)
+    pool = np.zeros((npages, 64, 3))
+    for b, n in enumerate(kv):
+        for p in range(n):
+            pool[om.paged_slot(bt, b, p, 64)] = (b, p, 1)
+    for b, n in enumerate(kv):
+        g = om.paged_gather(pool, bt, b, int(n), 64)
+        assert np.array_equal(g[:, 0], np.full(n, b)) and np.array_equal(g[:, 1], np.arange(n))
+
+
+def test_cache_row_is_norm_then_rope():
+    r = np.random.default_rng(17)
+    c_raw = r.standard_normal(32)
+    k_raw = r.standard_normal(8)
+    g = r.uniform(0.5, 1.5, 32)
+    row = om.cache_row(c_raw, k_raw, g, 5, 1e-6, 10000.0)
+    assert np.allclose(row[:32], _bf_rms(list(c_raw), list(g), 1e-6), rtol=1e-14)
+    assert np.allclose(row[32:], _bf_rope(list(k_raw), 5, 10000.0), rtol=1e-14, atol=1e-15)
+
+
+def test_decode_matches_prefill_last_rows():
+    # a decode step over rows produced by a prefill gives that prefill's last outputs
+    w, h = _rand_setup(21, L=8)
+    H, eps, base, scale = 3, 1e-6, 10000.0, 1.0 / math.sqrt(6)
+    o, rows = om.prefill(h, w, H, eps, base, scale)
+    q_c, q_r = om.query_path(h[6:], w["w_dq"], w["g_q"], w["w_uq"], w["w_qr"], np.array([6, 7]), H, eps, base)
+    od = om.decode([rows], [8], 2, q_c[None], q_r[None], w["w_uk"], w["w_uv"], rows.shape[1] - 2, scale)
+    assert _rel(od[0], o[6:]) <= 1e-13
+
+
+def test_prefill_with_past_rows_matches_whole():
+    w, h = _rand_setup(22, L=9)
+    H, eps, base, scale = 3, 1e-6, 10000.0, 1.0 / math.sqrt(6)
+    o_all, rows_all = om.prefill(h, w, H, eps, base, scale)
+    o2, rows2 = om.prefill(h[4:], w, H, eps, base, scale, start_pos=4, past_rows=rows_all[:4])
+    assert _rel(rows2, rows_all[4:]) <= 1e-14
+    assert _rel(o2, o_all[4:]) <= 1e-13
