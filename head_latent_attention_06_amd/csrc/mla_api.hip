@@ -1,0 +1,427 @@
+// C ABI of libmla: argument validation (before any launch), workspace
+// carving and the launch sequence of each entry point.  Declarations and the
+// contract are in include/mla.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+#include "mla_kernels.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int ATTN_SPLIT_PAGES = 1536;  // page ids one attention workgroup stages in LDS
+constexpr int DECODE_TARGET_ITEMS = 256;  // about one workgroup per CU for even batches
+constexpr int RAGGED_FACTOR = 4;          // the plan uses 4x as many chunks for ragged ones
+constexpr int MIN_CHUNK = 256;
+
+struct Carve {
+  unsigned char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((unsigned char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mla_status check_cfg(const mla_config* c, bool* bf16) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->n_heads <= 0 || c->d_head <= 0 || c->d_rope <= 0 || c->d_c <= 0 || c->d_cq <= 0 || c->d_model <= 0 ||
+      c->page_size <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!(c->softmax_scale > 0.f) || !(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return MLA_ERR_INVALID_ARG;
+  if (c->page_size % 32 != 0 || (c->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
+  if (c->dtype == MLA_BF16) {
+    *bf16 = true;
+    if (c->d_c != 512 || c->d_rope != 64 || c->n_heads % 32 != 0 || c->d_head % 64 != 0 || c->d_head > 512 ||
+        c->d_model % 64 != 0 || c->d_cq % 64 != 0)
+      return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+  }
+  if (c->dtype == MLA_F32) {
+    *bf16 = false;
+    if (c->d_c > 1024 || c->d_rope > 128 || c->d_head > 256) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+  }
+  return MLA_ERR_UNSUPPORTED;
+}
+
+mla_status check_cache(const mla_config* c, const mla_kv_cache* k) {
+  if (!k || !k->pool || !k->block_table || k->num_pages <= 0 || k->max_pages_per_seq <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(k->pool)) return MLA_ERR_INVALID_ARG;
+  (void)c;
+  return MLA_OK;
+}
+
+int32_t max_chunk_keys(const mla_config* c) {
+  const int64_t m = (int64_t)(ATTN_SPLIT_PAGES - 1) * c->page_size;
+  return (int32_t)(m > (1 << 30) ? (1 << 30) : m);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Upper bound on plan items for n_rows rows of at most max_kv visible keys.
+int64_t max_plan_items(const mla_config* c, int64_t n_rows, int32_t max_kv, int32_t target) {
+  const int64_t by_cap = n_rows * ceil_div(max_kv, max_chunk_keys(c));
+  const int64_t by_target = target > 0 ? n_rows + (int64_t)target * RAGGED_FACTOR : 0;
+  return by_target > by_cap ? by_target : by_cap;
+}
+
+// ----- workspace layouts --------------------------------------------------
+struct DecodeWs {
+  void *q_abs, *o_lat;
+  int32_t* plan;
+  float *part_acc, *part_ml;
+  int64_t max_items;
+};
+
+DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, int32_t max_kv, void* ws,
+                       size_t* total) {
+  Carve cv(ws);
+  DecodeWs d{};
+  const int64_t rows = (int64_t)B * s_q, H = c->n_heads, row = c->d_c + c->d_rope;
+  const size_t e = bf16 ? 2 : 4;
+  d.q_abs = cv.take(rows * H * row * e);
+  d.o_lat = cv.take(rows * H * c->d_c * e);
+  if (bf16) {
+    d.max_items = max_plan_items(c, rows, max_kv, DECODE_TARGET_ITEMS);
+    d.plan = (int32_t*)cv.take((rows + 3) * 4);
+    d.part_acc = (float*)cv.take(d.max_items * H * c->d_c * 4);
+    d.part_ml = (float*)cv.take(d.max_items * H * 2 * 4);
+  }
+  *total = cv.off;
+  return d;
+}
+
+struct PrefillWs {
+  float *kv_raw, *cq_raw, *qr_raw, *rope_cs, *part_acc, *part_ml;
+  void *cq, *qc, *q_abs, *o_lat;
+  int32_t* plan;
+  int64_t max_items;
+  bool split;
+};
+
+PrefillWs prefill_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, int32_t start_pos, void* ws,
+                         size_t* total) {
+  Carve cv(ws);
+  PrefillWs p{};
+  const int64_t T = (int64_t)B * L, H = c->n_heads, row = c->d_c + c->d_rope;
+  const size_t e = bf16 ? 2 : 4;
+  p.rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
+  p.kv_raw = (float*)cv.take(T * row * 4);
+  p.cq_raw = (float*)cv.take(T * c->d_cq * 4);
+  p.cq = cv.take(T * c->d_cq * e);
+  p.qc = cv.take(T * H * c->d_head * e);
+  p.qr_raw = (float*)cv.take(T * H * c->d_rope * 4);
+  p.q_abs = cv.take(T * H * row * e);
+  p.o_lat = cv.take(T * H * c->d_c * e);
+  if (bf16) {
+    const int32_t kv_end = start_pos + L;
+    p.split = kv_end > max_chunk_keys(c);
+    p.max_items = max_plan_items(c, T, kv_end, 0);
+    p.plan = (int32_t*)cv.take((T + 3) * 4);
+    if (p.split) {
+      p.part_acc = (float*)cv.take(p.max_items * H * c->d_c * 4);
+      p.part_ml = (float*)cv.take(p.max_items * H * 2 * 4);
+    }
+  }
+  *total = cv.off;
+  return p;
+}
+
+size_t project_kv_layout(const mla_config* c, int32_t B, int32_t L, void* ws, float** rope_cs, float** kv_raw) {
+  Carve cv(ws);
+  const int64_t T = (int64_t)B * L;
+  *rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
+  *kv_raw = (float*)cv.take(T * (c->d_c + c->d_rope) * 4);
+  return cv.off;
+}
+
+#define MLA_HIP(x)                          \
+  do {                                      \
+    if ((x) != hipSuccess) return MLA_ERR_HIP; \
+  } while (0)
+
+mla_status launch_gemm(bool bf16, const GemmArgs& g, hipStream_t st) {
+  MLA_HIP(bf16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st));
+  return MLA_OK;
+}
+
+GemmArgs gemm(const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc,
+              int64_t sC, int M, int N, int K, int batch, bool b_kn, bool out_bf16) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.strideA = sA;
+  g.B = B; g.ldb = ldb; g.strideB = sB;
+  g.B2 = nullptr; g.n_split = 0;
+  g.C = C; g.ldc = ldc; g.strideC = sC;
+  g.M = M; g.N = N; g.K = K; g.batch = batch;
+  g.b_kn = b_kn ? 1 : 0;
+  g.out_bf16 = out_bf16 ? 1 : 0;
+  return g;
+}
+
+// [c_raw ; k_raw] = [W^DKV ; W^KR] h, then the append of those rows.
+mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache* k, const mla_weights* w,
+                              const void* h, int32_t B, int32_t L, int32_t start_pos, float* rope_cs,
+                              float* kv_raw, hipStream_t st) {
+  const int64_t T = (int64_t)B * L;
+  const int row = c->d_c + c->d_rope;
+  MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, c->rope_base, st));
+  GemmArgs g = gemm(h, c->d_model, 0, w->w_dkv, c->d_model, 0, kv_raw, row, 0, (int)T, row, c->d_model, 1, false,
+                    false);
+  g.B2 = w->w_kr;
+  g.n_split = c->d_c;
+  if (launch_gemm(bf16, g, st) != MLA_OK) return MLA_ERR_HIP;
+  AppendArgs a{};
+  a.ckv = kv_raw; a.ld_ckv = row;
+  a.kr = kv_raw + c->d_c; a.ld_kr = row;
+  a.g_kv = w->g_kv;
+  a.seq_idx = nullptr; a.pos = nullptr;
+  a.n = (int32_t)T; a.n_seqs = B; a.L = L; a.start_pos = start_pos;
+  a.in_f32 = 1;
+  a.rope_cs = rope_cs;
+  a.pool = k->pool; a.num_pages = k->num_pages;
+  a.block_table = k->block_table; a.max_pages = k->max_pages_per_seq; a.page_size = c->page_size;
+  a.err_flags = k->err_flags;
+  a.d_c = c->d_c; a.d_rope = c->d_rope;
+  a.eps = c->rms_eps; a.rope_base = c->rope_base;
+  a.bf16_cache = bf16 ? 1 : 0;
+  MLA_HIP(launch_append(a, st));
+  return MLA_OK;
+}
+
+AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_abs, const int32_t* kv_lens,
+                   int32_t uniform_kv, int32_t max_kv, int32_t B, int32_t s_q) {
+  AttnArgs a{};
+  a.q_abs = q_abs;
+  a.pool = k->pool;
+  a.block_table = k->block_table;
+  a.num_pages = k->num_pages;
+  a.max_pages = k->max_pages_per_seq;
+  a.page_size = c->page_size;
+  a.err_flags = k->err_flags;
+  a.kv_lens = kv_lens;
+  a.uniform_kv = uniform_kv;
+  a.max_kv = max_kv;
+  a.B = B;
+  a.s_q = s_q;
+  a.H = c->n_heads;
+  a.d_c = c->d_c;
+  a.d_rope = c->d_rope;
+  a.scale = c->softmax_scale;
+  return a;
+}
+
+// Attention + merge + W^UV for rows whose absorbed queries are in q_abs.
+mla_status attend(const mla_config* c, bool bf16, AttnArgs a, int32_t* plan, int64_t max_items, int32_t target,
+                  bool need_merge, float* part_acc, float* part_ml, void* o_lat, const void* w_uv, void* out,
+                  hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.s_q;
+  a.o_lat = o_lat;
+  if (bf16) {
+    a.plan = plan;
+    a.max_items = (int32_t)max_items;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    MLA_HIP(launch_attn_plan(a, plan, target, MIN_CHUNK, max_chunk_keys(c) / 32 * 32, st));
+    MLA_HIP(launch_attn_bf16(a, st));
+    if (need_merge) MLA_HIP(launch_merge_bf16(a, st));
+  } else {
+    MLA_HIP(launch_attn_f32(a, st));
+  }
+  // o[t, i, :] = W_i^UV o_lat[t, i, :]
+  GemmArgs g = gemm(o_lat, (int64_t)c->n_heads * c->d_c, c->d_c, w_uv, c->d_c, (int64_t)c->d_head * c->d_c, out,
+                    (int64_t)c->n_heads * c->d_head, c->d_head, (int)rows, c->d_head, c->d_c, c->n_heads, false, bf16);
+  return launch_gemm(bf16, g, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive size or misaligned pointer";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not implemented";
+    case MLA_ERR_OUT_OF_RANGE: return "MLA_ERR_OUT_OF_RANGE: length exceeds the cache";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch or runtime call failed";
+  }
+  return "unknown mla_status";
+}
+
+mla_status mla_cache_append(const mla_config* cfg, const mla_kv_cache* cache, const void* ckv_raw,
+                            const void* kr_raw, const void* g_kv, const int32_t* seq_idx, const int32_t* pos,
+                            int32_t n, int32_t n_seqs, void* stream) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if ((s = check_cache(cfg, cache)) != MLA_OK) return s;
+  if (n < 0 || n_seqs <= 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!ckv_raw || !kr_raw || !g_kv || !seq_idx || !pos) return MLA_ERR_INVALID_ARG;
+  AppendArgs a{};
+  a.ckv = ckv_raw; a.ld_ckv = cfg->d_c;
+  a.kr = kr_raw; a.ld_kr = cfg->d_rope;
+  a.g_kv = g_kv;
+  a.seq_idx = seq_idx; a.pos = pos;
+  a.n = n; a.n_seqs = n_seqs; a.L = 1; a.start_pos = 0;
+  a.in_f32 = bf16 ? 0 : 1;
+  a.rope_cs = nullptr;
+  a.pool = cache->pool; a.num_pages = cache->num_pages;
+  a.block_table = cache->block_table; a.max_pages = cache->max_pages_per_seq; a.page_size = cfg->page_size;
+  a.err_flags = cache->err_flags;
+  a.d_c = cfg->d_c; a.d_rope = cfg->d_rope;
+  a.eps = cfg->rms_eps; a.rope_base = cfg->rope_base;
+  a.bf16_cache = bf16 ? 1 : 0;
+  return launch_append(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_project_kv_workspace_size(const mla_config* cfg, int32_t B, int32_t L, size_t* bytes) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if (!bytes || B < 0 || L < 0) return MLA_ERR_INVALID_ARG;
+  float *a, *b;
+  *bytes = project_kv_layout(cfg, B, L, nullptr, &a, &b);
+  return MLA_OK;
+}
+
+mla_status mla_project_kv(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w, const void* h,
+                          int32_t B, int32_t L, int32_t start_pos, void* ws, size_t ws_bytes, void* stream) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if ((s = check_cache(cfg, cache)) != MLA_OK) return s;
+  if (B < 0 || L < 0 || start_pos < 0) return MLA_ERR_INVALID_ARG;
+  if (B == 0 || L == 0) return MLA_OK;
+  if (!w || !w->w_dkv || !w->w_kr || !w->g_kv || !h || !ws) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w->w_dkv) || !aligned16(w->w_kr) || !aligned16(ws)) return MLA_ERR_INVALID_ARG;
+  if (B > (1 << 20) || (int64_t)start_pos + L > (int64_t)cache->max_pages_per_seq * cfg->page_size)
+    return MLA_ERR_OUT_OF_RANGE;
+  float *rope_cs, *kv_raw;
+  if (project_kv_layout(cfg, B, L, ws, &rope_cs, &kv_raw) > ws_bytes) return MLA_ERR_WORKSPACE;
+  return project_and_append(cfg, bf16, cache, w, h, B, L, start_pos, rope_cs, kv_raw, (hipStream_t)stream);
+}
+
+mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t L, int32_t start_pos,
+                                      size_t* bytes) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if (!bytes || B < 0 || L < 0 || start_pos < 0) return MLA_ERR_INVALID_ARG;
+  prefill_layout(cfg, bf16, B, L, start_pos, nullptr, bytes);
+  return MLA_OK;
+}
+
+mla_status mla_prefill(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w, const void* h,
+                       int32_t B, int32_t L, int32_t start_pos, void* out, void* ws, size_t ws_bytes, void* stream) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if ((s = check_cache(cfg, cache)) != MLA_OK) return s;
+  if (B < 0 || L < 0 || start_pos < 0) return MLA_ERR_INVALID_ARG;
+  if (B == 0 || L == 0) return MLA_OK;
+  if (!w || !h || !out || !ws || !w->w_dq || !w->g_q || !w->w_uq || !w->w_qr || !w->w_dkv || !w->g_kv ||
+      !w->w_kr || !w->w_uk || !w->w_uv)
+    return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {h, out, ws, w->w_dq, w->w_uq, w->w_qr, w->w_dkv, w->w_kr, w->w_uk, w->w_uv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
+  const int64_t kv_end = (int64_t)start_pos + L;
+  if (kv_end > (int64_t)cache->max_pages_per_seq * cfg->page_size || kv_end > (1 << 30)) return MLA_ERR_OUT_OF_RANGE;
+  if ((int64_t)B * L > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  size_t need;
+  PrefillWs p = prefill_layout(cfg, bf16, B, L, start_pos, ws, &need);
+  if (need > ws_bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = B * L, H = cfg->n_heads, row = cfg->d_c + cfg->d_rope;
+  // steps (5), (7): cached latents, then the append
+  if ((s = project_and_append(cfg, bf16, cache, w, h, B, L, start_pos, p.rope_cs, p.kv_raw, st)) != MLA_OK) return s;
+  // step (1): c^Q = RMSNorm(W^DQ h)
+  if ((s = launch_gemm(bf16, gemm(h, cfg->d_model, 0, w->w_dq, cfg->d_model, 0, p.cq_raw, cfg->d_cq, 0, T,
+                                  cfg->d_cq, cfg->d_model, 1, false, false), st)) != MLA_OK)
+    return s;
+  MLA_HIP(launch_rmsnorm(p.cq_raw, cfg->d_cq, w->g_q, p.cq, cfg->d_cq, T, cfg->d_cq, cfg->rms_eps, bf16, st));
+  // step (2): q^C = W^UQ c^Q
+  if ((s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_uq, cfg->d_cq, 0, p.qc, (int64_t)H * cfg->d_head, 0, T,
+                                  H * cfg->d_head, cfg->d_cq, 1, false, bf16), st)) != MLA_OK)
+    return s;
+  // step (3): q^R = RoPE(W^QR c^Q), written next to the absorbed query
+  if ((s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_qr, cfg->d_cq, 0, p.qr_raw, (int64_t)H * cfg->d_rope, 0,
+                                  T, H * cfg->d_rope, cfg->d_cq, 1, false, false), st)) != MLA_OK)
+    return s;
+  MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.q_abs, row, cfg->d_c, T, H, cfg->d_rope, bf16, st));
+  // absorption: q_lat_i = W_i^UK^T q^C_i  (batched over heads, W_i^UK given [d_h, d_c])
+  if ((s = launch_gemm(bf16, gemm(p.qc, (int64_t)H * cfg->d_head, cfg->d_head, w->w_uk, cfg->d_c,
+                                  (int64_t)cfg->d_head * cfg->d_c, p.q_abs, (int64_t)H * row, row, T, cfg->d_c,
+                                  cfg->d_head, H, true, bf16), st)) != MLA_OK)
+    return s;
+  // step (10) in absorbed form over rows [0, start_pos + t]
+  AttnArgs a = attn_args(cfg, cache, p.q_abs, nullptr, (int32_t)kv_end, (int32_t)kv_end, B, L);
+  a.longest_first = 1;
+  return attend(cfg, bf16, a, p.plan, p.max_items, 0, p.split, p.part_acc, p.part_ml, p.o_lat, w->w_uv, out, st);
+}
+
+mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t s_q, int32_t max_kv_len,
+                                     size_t* bytes) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if (!bytes || B < 0 || s_q < 0 || max_kv_len < 0) return MLA_ERR_INVALID_ARG;
+  decode_layout(cfg, bf16, B, s_q, max_kv_len, nullptr, bytes);
+  return MLA_OK;
+}
+
+int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t s_q, int32_t max_kv_len) {
+  bool bf16;
+  if (check_cfg(cfg, &bf16) != MLA_OK || B <= 0 || s_q <= 0 || max_kv_len <= 0) return 0;
+  if (!bf16) return 1;
+  return (int32_t)max_plan_items(cfg, (int64_t)B * s_q, max_kv_len, DECODE_TARGET_ITEMS);
+}
+
+mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens, int32_t max_kv_len,
+                      int32_t B, int32_t s_q, const void* q_nope, const void* q_pe, const void* w_uk,
+                      const void* w_uv, void* out, void* ws, size_t ws_bytes, void* stream) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if ((s = check_cache(cfg, cache)) != MLA_OK) return s;
+  if (B < 0 || s_q < 0) return MLA_ERR_INVALID_ARG;
+  if (B == 0 || s_q == 0) return MLA_OK;
+  if (!kv_lens || !q_nope || !q_pe || !w_uk || !w_uv || !out || !ws) return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, out, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (max_kv_len < s_q) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)max_kv_len > (int64_t)cache->max_pages_per_seq * cfg->page_size || max_kv_len > (1 << 30))
+    return MLA_ERR_OUT_OF_RANGE;
+  if ((int64_t)B * s_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  size_t need;
+  DecodeWs d = decode_layout(cfg, bf16, B, s_q, max_kv_len, ws, &need);
+  if (need > ws_bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int rows = B * s_q, H = cfg->n_heads, row = cfg->d_c + cfg->d_rope;
+  // absorption: Q_abs[t, i, :d_c] = W_i^UK^T q^C[t, i]; Q_abs[t, i, d_c:] = q^R[t, i]
+  if ((s = launch_gemm(bf16, gemm(q_nope, (int64_t)H * cfg->d_head, cfg->d_head, w_uk, cfg->d_c,
+                                  (int64_t)cfg->d_head * cfg->d_c, d.q_abs, (int64_t)H * row, row, rows, cfg->d_c,
+                                  cfg->d_head, H, true, bf16), st)) != MLA_OK)
+    return s;
+  MLA_HIP(launch_copy_heads(q_pe, d.q_abs, row, cfg->d_c, rows, H, cfg->d_rope, bf16 ? 2 : 4, st));
+  AttnArgs a = attn_args(cfg, cache, d.q_abs, kv_lens, 0, max_kv_len, B, s_q);
+  a.longest_first = 0;
+  return attend(cfg, bf16, a, d.plan, d.max_items, DECODE_TARGET_ITEMS, true, d.part_acc, d.part_ml, d.o_lat, w_uv,
+                out, st);
+}
+
+}  // extern "C"

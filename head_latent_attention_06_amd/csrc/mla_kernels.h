@@ -1,0 +1,101 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Latent attention of query rows over a sequence's paged cache.  Query row
+// r = b*s_q + s sits at position kv_len(b) - s_q + s and sees cache rows
+// [0, that position].  A device work plan cuts every row's visible keys into
+// chunks of `chunk` keys; each (chunk, head group of 128) is one workgroup.
+//
+// Plan layout (int32, device): [0] n_items, [1] chunk, [2 + r] first item of
+// row r for r = 0 .. n_rows (row r owns items plan[2+r] .. plan[3+r]-1).
+struct AttnArgs {
+  const void* q_abs;          // [n_rows, H, d_c + d_rope]: [W_i^UK^T q^C ; q^R]
+  const void* pool;           // [num_pages, page_size, d_c + d_rope]
+  const int32_t* block_table; // [B, max_pages]
+  int64_t num_pages;
+  int32_t max_pages, page_size;
+  int32_t* err_flags;         // may be null
+  const int32_t* kv_lens;     // [B] or null (then uniform_kv)
+  int32_t uniform_kv, max_kv;
+  int32_t B, s_q, H;
+  int32_t d_c, d_rope;        // f32 path only; the bf16 kernel is fixed at 512 / 64
+  const int32_t* plan;        // work plan (above)
+  int32_t max_items;          // grid size (upper bound on plan[0])
+  int32_t longest_first;      // run items in reverse order (rows with most keys last in the plan)
+  float scale;                // softmax scale
+  float* part_acc;            // [max_items, H, d_c]  rows split into several chunks
+  float* part_ml;             // [max_items, H, 2]
+  void* o_lat;                // [n_rows, H, d_c]
+};
+
+// Plan: target_items > 0 balances chunks to about that many items (more for
+// ragged batches); target_items == 0 uses max_chunk.  Chunks are multiples of
+// 32 keys within [min_chunk, max_chunk].
+hipError_t launch_attn_plan(const AttnArgs& a, int32_t* plan, int32_t target_items, int32_t min_chunk,
+                            int32_t max_chunk, hipStream_t st);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_merge_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
+
+// Batched GEMM C[z][m][n] = sum_k A[z][m][k] * B[z](k, n) with fp32 accumulation.
+// B(k, n) = B[n*ldb + k] (b_kn = false: weights stored [out, in]) or
+//           B[k*ldb + n] (b_kn = true).  When B2 is set, rows n >= n_split of a
+// [N, K] weight come from B2 (row n - n_split); b_kn must be false then.
+struct GemmArgs {
+  const void* A; int64_t lda, strideA;
+  const void* B; int64_t ldb, strideB;
+  const void* B2; int32_t n_split;
+  void* C; int64_t ldc, strideC;
+  int32_t M, N, K, batch;
+  int32_t b_kn;
+  int32_t out_bf16;           // bf16 path: store C as bf16 (else fp32)
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t st);
+
+// Cache append: row i -> [RMSNorm(ckv[i]) ; RoPE(kr[i], pos)] into its page slot.
+// seq_idx / pos may be null: then sequence = i / L and pos = start_pos + i % L.
+struct AppendArgs {
+  const void* ckv; int64_t ld_ckv;   // [n, d_c] rows, leading dimension in elements
+  const void* kr;  int64_t ld_kr;    // [n, d_rope]
+  const void* g_kv;
+  const int32_t* seq_idx; const int32_t* pos;
+  int32_t n, n_seqs, L, start_pos;
+  int32_t in_f32;                    // ckv / kr are fp32 (else cfg dtype)
+  const float* rope_cs;              // optional [L, d_rope/2, 2] cos/sin for implicit positions
+  void* pool; int64_t num_pages;
+  const int32_t* block_table; int32_t max_pages, page_size;
+  int32_t* err_flags;
+  int32_t d_c, d_rope;
+  float eps, rope_base;
+  int32_t bf16_cache;                // cache dtype is bf16 (else fp32)
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+// cos / sin of pos * theta_p for positions start_pos .. start_pos + L - 1,
+// computed in double precision: out [L, d_rope/2, 2] fp32.
+hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, float base,
+                             hipStream_t st);
+
+// RMSNorm of fp32 rows into the storage dtype: out[r] = x[r] / rms(x[r]) * g.
+hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out, int64_t ldo,
+                          int32_t rows, int32_t width, float eps, int32_t bf16_io, hipStream_t st);
+
+// RoPE of fp32 per-head rows x [T, H, d_rope] with a cos/sin table (row t uses
+// table row t % table_rows) into out[t, h, out_off ...] of row stride ld_out
+// per head.
+hipError_t launch_rope_heads(const float* x, const float* cs, int32_t table_rows, void* out,
+                             int64_t ld_out, int32_t out_off, int32_t T, int32_t H, int32_t d_rope,
+                             int32_t bf16_out, hipStream_t st);
+
+// Copy per-head rows src [T, H, w] into dst[t, h, dst_off ...] (row stride ld_dst).
+hipError_t launch_copy_heads(const void* src, void* dst, int64_t ld_dst, int32_t dst_off, int32_t T,
+                             int32_t H, int32_t w, int32_t elem_bytes, hipStream_t st);
+
+}  // namespace mla

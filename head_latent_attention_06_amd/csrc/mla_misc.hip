@@ -1,0 +1,208 @@
+// Element-wise parts of the MLA layer: the cache append (RMSNorm of c^KV,
+// RoPE of k^R, paged scatter), the RMSNorm of c^Q, RoPE of q^R and packing.
+//
+// Definitions (notes page "【论文解读】DeepSeek-V3"):
+//  * RMSNorm after each compressed latent (section 二(二)1):
+//      y = x / sqrt(mean(x^2) + eps) * g
+//  * RoPE (section 一(一)3): each adjacent pair (x_2p, x_2p+1) is rotated by
+//    the 2x2 block [[cos, -sin], [sin, cos]] at angle pos * theta_p, with
+//    theta_p = base^(-2p/d_rope) (the frequency formula of the hnwysp.cn
+//    digest, section 4.3).  Angles are formed and reduced in double precision:
+//    at position 131072 a float angle would already be off by ~1e-2 rad.
+//  * Only [c^KV ; k^R] is cached per token (end of section 一(一)3); token p
+//    of sequence b lives at slot p % page_size of page block_table[b][p / page_size].
+#include <math.h>
+
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int FLAG_BAD_PAGE = 1, FLAG_BAD_POS = 2, FLAG_BAD_SEQ = 8;
+
+__device__ __forceinline__ void rope_cos_sin(int pos, int p, int d_rope, double base, float& c, float& s) {
+  const double theta = pow(base, -2.0 * (double)p / (double)d_rope);
+  const double ang = (double)pos * theta;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_as_f32(const void* p, int64_t i) {
+  return to_f32(((const T*)p)[i]);
+}
+
+// One wave per appended token.
+template <typename TIN, typename TOUT>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  int b, pos;
+  if (a.seq_idx) {
+    b = a.seq_idx[i];
+    pos = a.pos[i];
+  } else {
+    b = i / a.L;
+    pos = a.start_pos + i % a.L;
+  }
+  if (b < 0 || b >= a.n_seqs) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_SEQ);
+    return;
+  }
+  const int pidx = pos >= 0 ? pos / a.page_size : -1;
+  if (pidx < 0 || pidx >= a.max_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_POS);
+    return;
+  }
+  const int page = a.block_table[(int64_t)b * a.max_pages + pidx];
+  if (page < 0 || (int64_t)page >= a.num_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
+    return;
+  }
+  const int row = a.d_c + a.d_rope;
+  TOUT* dst = (TOUT*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * row;
+  const int64_t ci = (int64_t)i * a.ld_ckv, ki = (int64_t)i * a.ld_kr;
+
+  // RMSNorm of the latent
+  float ss = 0.f;
+  for (int d = lane; d < a.d_c; d += 64) {
+    const float x = ld_as_f32<TIN>(a.ckv, ci + d);
+    ss += x * x;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)a.d_c + a.eps);
+  for (int d = lane; d < a.d_c; d += 64) {
+    const float x = ld_as_f32<TIN>(a.ckv, ci + d);
+    const float g = ld_as_f32<TOUT>(a.g_kv, d);
+    dst[d] = from_f32<TOUT>(x * inv * g);
+  }
+  // RoPE of the shared decoupled key
+  for (int p = lane; p < a.d_rope / 2; p += 64) {
+    float c, s;
+    if (a.rope_cs) {
+      const float* cs = a.rope_cs + ((int64_t)(i % a.L) * (a.d_rope / 2) + p) * 2;
+      c = cs[0];
+      s = cs[1];
+    } else {
+      rope_cos_sin(pos, p, a.d_rope, (double)a.rope_base, c, s);
+    }
+    const float x0 = ld_as_f32<TIN>(a.kr, ki + 2 * p), x1 = ld_as_f32<TIN>(a.kr, ki + 2 * p + 1);
+    dst[a.d_c + 2 * p] = from_f32<TOUT>(c * x0 - s * x1);
+    dst[a.d_c + 2 * p + 1] = from_f32<TOUT>(s * x0 + c * x1);
+  }
+}
+
+__global__ void rope_table_kernel(float* out, int L, int start_pos, int d_rope, float base) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = d_rope / 2;
+  if (idx >= (int64_t)L * half) return;
+  const int t = (int)(idx / half), p = (int)(idx % half);
+  float c, s;
+  rope_cos_sin(start_pos + t, p, d_rope, (double)base, c, s);
+  out[idx * 2] = c;
+  out[idx * 2 + 1] = s;
+}
+
+// One wave per row.
+template <typename TOUT>
+__global__ __launch_bounds__(64) void rmsnorm_kernel(const float* x, int64_t ldx, const void* g, TOUT* out,
+                                                     int64_t ldo, int width, float eps) {
+  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* xr = x + r * ldx;
+  float ss = 0.f;
+  for (int d = lane; d < width; d += 64) ss += xr[d] * xr[d];
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)width + eps);
+  for (int d = lane; d < width; d += 64) out[r * ldo + d] = from_f32<TOUT>(xr[d] * inv * to_f32(((const TOUT*)g)[d]));
+}
+
+// One thread per rotated pair.
+template <typename TOUT>
+__global__ void rope_heads_kernel(const float* x, const float* cs, int table_rows, TOUT* out, int64_t ld_out,
+                                  int out_off, int64_t T, int H, int d_rope) {
+  const int half = d_rope / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * H * half) return;
+  const int p = (int)(idx % half);
+  const int64_t th = idx / half;  // t * H + h
+  const int64_t t = th / H;
+  const float* c = cs + ((t % table_rows) * half + p) * 2;
+  const float x0 = x[th * d_rope + 2 * p], x1 = x[th * d_rope + 2 * p + 1];
+  TOUT* o = out + th * ld_out + out_off;
+  o[2 * p] = from_f32<TOUT>(c[0] * x0 - c[1] * x1);
+  o[2 * p + 1] = from_f32<TOUT>(c[1] * x0 + c[0] * x1);
+}
+
+// One thread per 4-byte word of a head row.
+__global__ void copy_heads_kernel(const uint32_t* src, unsigned char* dst, int64_t ld_dst_bytes, int dst_off_bytes,
+                                  int64_t rows, int words) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * words) return;
+  const int64_t r = idx / words;
+  const int wd = (int)(idx % words);
+  *(uint32_t*)(dst + r * ld_dst_bytes + dst_off_bytes + 4 * wd) = src[idx];
+}
+
+unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid((unsigned)a.n), block(64);
+  if (a.bf16_cache) {
+    if (a.in_f32)
+      hipLaunchKernelGGL((append_kernel<float, bf16>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((append_kernel<bf16, bf16>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((append_kernel<float, float>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, float base, hipStream_t st) {
+  const int64_t n = (int64_t)L * (d_rope / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, out, L, start_pos, d_rope, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out, int64_t ldo, int32_t rows,
+                          int32_t width, float eps, int32_t bf16_io, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (bf16_io)
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(rows), dim3(64), 0, st, x, ldx, g, (bf16*)out, ldo, width, eps);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<float>), dim3(rows), dim3(64), 0, st, x, ldx, g, (float*)out, ldo, width, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_heads(const float* x, const float* cs, int32_t table_rows, void* out, int64_t ld_out,
+                             int32_t out_off, int32_t T, int32_t H, int32_t d_rope, int32_t bf16_out, hipStream_t st) {
+  const int64_t n = (int64_t)T * H * (d_rope / 2);
+  if (n <= 0) return hipSuccess;
+  if (bf16_out)
+    hipLaunchKernelGGL((rope_heads_kernel<bf16>), dim3(blocks_for(n, 256)), dim3(256), 0, st, x, cs, table_rows,
+                       (bf16*)out, ld_out, out_off, (int64_t)T, H, d_rope);
+  else
+    hipLaunchKernelGGL((rope_heads_kernel<float>), dim3(blocks_for(n, 256)), dim3(256), 0, st, x, cs, table_rows,
+                       (float*)out, ld_out, out_off, (int64_t)T, H, d_rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_heads(const void* src, void* dst, int64_t ld_dst, int32_t dst_off, int32_t T, int32_t H,
+                             int32_t w, int32_t elem_bytes, hipStream_t st) {
+  const int64_t rows = (int64_t)T * H;
+  const int words = w * elem_bytes / 4;
+  if (rows <= 0 || words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_heads_kernel, dim3(blocks_for(rows * words, 256)), dim3(256), 0, st, (const uint32_t*)src,
+                     (unsigned char*)dst, ld_dst * elem_bytes, dst_off * elem_bytes, rows, words);
+  return hipGetLastError();
+}
+
+}  // namespace mla

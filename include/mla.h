@@ -1,0 +1,182 @@
+/*
+ * mla.h -- C ABI of libmla, Multi-head Latent Attention (MLA) for AMD MI355X (gfx950).
+ *
+ * The operations are those of the notes page "【论文解读】DeepSeek-V3"
+ * (wkq9411.github.io), section 一(一) "多头潜在注意力MLA":
+ *   c^KV = W^DKV h,  k^C = W^UK c^KV,  v^C = W^UV c^KV              (section 2)
+ *   c^Q  = W^DQ h,   q^C = W^UQ c^Q                                  (section 2)
+ *   q^R  = RoPE(W^QR c^Q) per head,  k^R = RoPE(W^KR h) shared        (section 3)
+ *   o_{t,i} = sum_{j<=t} Softmax_j(q_{t,i} . k_{j,i} / sqrt(d_h + d_h^R)) v_{j,i}
+ * with q_{t,i} = [q^C_{t,i}; q^R_{t,i}] and k_{j,i} = [k^C_{j,i}; k^R_j]
+ * (the ten-step "完整计算过程" list), and an RMSNorm after each compressed
+ * latent (section 二(二)1).  Only c^KV and k^R are cached per token (end of
+ * section 一(一)3).  The library computes attention in the absorbed form of
+ * the 【思考】 passage on absorption: W_i^UK is folded into the query
+ * (q_lat = W_i^UK^T q^C_i, score = q_lat . c_j + q^R_i . k^R_j) and W_i^UV is
+ * applied after the weighted sum of latents (o_i = W_i^UV sum_j a_j c_j).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
+ *    owns and allocates every buffer (cache pool, workspace, outputs); the
+ *    library never allocates, frees or synchronises, and keeps no mutable
+ *    global state, so calls on different streams may run concurrently as long
+ *    as they touch disjoint buffers.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  MLA_OK means "enqueued".
+ *  - Argument, shape and dtype errors are detected on the host BEFORE any
+ *    launch, so a call that returns an error has written nothing.  A launch
+ *    failure returns MLA_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Weights are row-major [out, in] (y = W x); head i owns rows
+ *    [i*w, (i+1)*w) of a per-head projection of width w.
+ *  - MLA_BF16: bf16 storage, fp32 accumulation; the hand-written MFMA kernels
+ *    serve d_c = 512, d_rope = 64, d_head = 128 and n_heads a multiple of 32
+ *    (DeepSeek-V3 shapes).  MLA_F32: fp32 end to end, any small shape
+ *    (d_c <= 1024, d_rope <= 128, d_head <= 256, even d_rope).  Other
+ *    combinations return MLA_ERR_UNSUPPORTED.
+ *  - Pointers must be 16-byte aligned; row widths are in elements.
+ *  - Positions are 0-based absolute token positions within a sequence.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misalignment */
+  MLA_ERR_UNSUPPORTED = 2,  /* shape / dtype combination not implemented   */
+  MLA_ERR_OUT_OF_RANGE = 3, /* a host-visible length exceeds the cache      */
+  MLA_ERR_WORKSPACE = 4,    /* workspace smaller than *_workspace_size()    */
+  MLA_ERR_HIP = 5           /* a HIP launch or runtime call failed          */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Layer dimensions (host struct).  Names follow the notes page's symbols. */
+typedef struct {
+  int32_t n_heads;     /* n_h                                              */
+  int32_t d_head;      /* d_h                                              */
+  int32_t d_rope;      /* d_h^R, even                                      */
+  int32_t d_c;         /* KV latent width d_c                              */
+  int32_t d_cq;        /* query latent width d_c'                          */
+  int32_t d_model;     /* hidden width d                                   */
+  int32_t page_size;   /* tokens per cache page; a multiple of 32          */
+  float softmax_scale; /* normally 1/sqrt(d_head + d_rope)                 */
+  float rope_base;     /* theta_p = rope_base^(-2p/d_rope)                 */
+  float rms_eps;       /* RMSNorm epsilon                                  */
+  int32_t dtype;       /* mla_dtype                                        */
+} mla_config;
+
+/* Paged latent cache (host struct holding device pointers).
+ *  pool        [num_pages, page_size, d_c + d_rope] in cfg->dtype.  Token p
+ *              of sequence b lives at pool[block_table[b*max_pages_per_seq
+ *              + p/page_size]][p % page_size]; its row is c^KV (RMSNorm'd,
+ *              d_c values) followed by k^R (rotated, d_rope values).
+ *  block_table [n_seqs, max_pages_per_seq] int32 page ids.
+ *  err_flags   optional int32 word (may be NULL).  Kernels that meet a page
+ *              id outside [0, num_pages), a position beyond the table, or a
+ *              length beyond the caller's bound OR a bit into it and skip the
+ *              offending row (no out-of-bounds access); see MLA_FLAG_*. */
+typedef struct {
+  void* pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_pages_per_seq;
+  int32_t* err_flags;
+} mla_kv_cache;
+
+#define MLA_FLAG_BAD_PAGE 1 /* block-table entry outside [0, num_pages)        */
+#define MLA_FLAG_BAD_POS 2  /* position < 0 or beyond max_pages_per_seq pages  */
+#define MLA_FLAG_BAD_LEN 4  /* kv_len < s_q or kv_len > max_kv_len              */
+#define MLA_FLAG_BAD_SEQ 8  /* append seq_idx outside [0, n_seqs)              */
+
+/* Layer weights (host struct holding device pointers), all cfg->dtype.
+ *  w_dq [d_cq, d_model]          W^DQ     g_q  [d_cq]   RMSNorm gain of c^Q
+ *  w_uq [n_heads*d_head, d_cq]   W^UQ     w_qr [n_heads*d_rope, d_cq]  W^QR
+ *  w_dkv [d_c, d_model]          W^DKV    g_kv [d_c]    RMSNorm gain of c^KV
+ *  w_kr [d_rope, d_model]        W^KR (shared decoupled key)
+ *  w_uk, w_uv [n_heads*d_head, d_c]   W^UK, W^UV */
+typedef struct {
+  const void *w_dq, *g_q, *w_uq, *w_qr, *w_dkv, *g_kv, *w_kr, *w_uk, *w_uv;
+} mla_weights;
+
+/* Version of this interface (MLA_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Cache append (section 一(一)3: only c^KV and k^R are cached; section
+ * 二(二)1: RMSNorm after the compressed latent).  For each i < n, writes
+ *   [ RMSNorm(ckv_raw[i]; g_kv, rms_eps) ; RoPE(kr_raw[i], pos[i]) ]
+ * to the slot of token pos[i] of sequence seq_idx[i].
+ *  ckv_raw [n, d_c], kr_raw [n, d_rope] (before rotation), g_kv [d_c]: cfg->dtype.
+ *  seq_idx, pos [n] int32 (device).  n_seqs bounds seq_idx (rows of the
+ *  block table).  n == 0 is a no-op.  Rows that two i share are written in
+ *  unspecified order. */
+mla_status mla_cache_append(const mla_config* cfg, const mla_kv_cache* cache,
+                            const void* ckv_raw, const void* kr_raw, const void* g_kv,
+                            const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                            int32_t n_seqs, void* stream);
+
+/* Down-projection of the cached latents, then append (steps (5) and (7) of the
+ * complete computation): for token t of sequence b at position start_pos + t,
+ *   [c_raw ; k_raw] = [W^DKV ; W^KR] h[b, t]   (one GEMM, fp32 accumulation)
+ * followed by the append above.  h [B, L, d_model].  Uses the workspace of
+ * mla_project_kv_workspace_size(). */
+mla_status mla_project_kv_workspace_size(const mla_config* cfg, int32_t B, int32_t L, size_t* bytes);
+mla_status mla_project_kv(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
+                          const void* h, int32_t B, int32_t L, int32_t start_pos, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Causal prefill (all ten steps): sequences b < B hold L new tokens at
+ * positions [start_pos, start_pos + L).  Appends their rows to the cache
+ * (block-table row b), then computes for every new token t and head i
+ *   o[b, t, i, :] = W_i^UV sum_{j <= start_pos+t} a_j c_j   (d_head values)
+ * over all cached rows of sequence b (rows [0, start_pos) must already be
+ * present).  h [B, L, d_model]; out [B, L, n_heads, d_head]; both cfg->dtype.
+ * The output stops at o (W^O is not applied). */
+mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t L, int32_t start_pos,
+                                      size_t* bytes);
+mla_status mla_prefill(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
+                       const void* h, int32_t B, int32_t L, int32_t start_pos, void* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Decode step over the paged cache (split-context flash decoding).  Sequence
+ * b < B has kv_lens[b] cached rows, the last s_q of which are this step's
+ * tokens; query s sits at position kv_lens[b] - s_q + s and attends to rows
+ * j <= that position.
+ *  kv_lens [B] int32 (device); max_kv_len (host) bounds every kv_lens[b] and
+ *          sizes the split plan.
+ *  q_nope [B, s_q, n_heads, d_head]   q^C
+ *  q_pe   [B, s_q, n_heads, d_rope]   q^R, already rotated
+ *  w_uk, w_uv [n_heads*d_head, d_c]
+ *  out    [B, s_q, n_heads, d_head]
+ * The workspace holds the absorbed queries, the split partials and the merged
+ * latent outputs; size it with mla_decode_workspace_size(). */
+mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t s_q,
+                                     int32_t max_kv_len, size_t* bytes);
+mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                      int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope,
+                      const void* q_pe, const void* w_uk, const void* w_uv, void* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Upper bound on the attention work items (split partial slots) mla_decode
+ * plans for these sizes; the device plan cuts each query row's visible keys
+ * into chunks from the actual kv_lens.  Host helper for tests and sizing;
+ * returns 0 for invalid arguments. */
+int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t s_q, int32_t max_kv_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,88 @@
+"""Decode parity: the HIP path through the C ABI against the float64 oracle.
+
+Workloads are seeded synthetic inputs (``mla_inputs``) with the decode
+configurations' shapes; the oracle materialises per-head k and v explicitly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from mla_testutil import BF16_TOL, decode_setup, host, oracle_decode, rel_l2, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(config_id, contexts, s_q, shape=mi.V3):
+    return mi.decode_inputs(config_id, shape, contexts, s_q)
+
+
+@pytest.mark.parametrize("contexts,s_q", [
+    ([0, 1, 31, 32, 33, 63, 64, 65, 100, 300], 1),   # ragged tails around tile/page edges
+    ([0, 5, 127, 129, 700], 2),                       # two causal queries per sequence
+    ([2047], 1),                                      # one long row, many chunks
+])
+def test_decode_small_full_compare(contexts, s_q):
+    print(f"[decode small] contexts={contexts} s_q={s_q}", flush=True)
+    inp = _case(101, contexts, s_q)
+    cfg, cache, bt, t = decode_setup(inp)
+    out = run_decode(cfg, cache, t, int(inp.kv_lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle_decode(inp)
+    got = host(out)
+    assert np.isfinite(got).all()
+    err = rel_l2(got, ref)
+    print(f"rel_l2={err:.3e}")
+    assert err <= BF16_TOL
+    for b in range(len(contexts)):  # every sequence on its own, not just the batch
+        assert rel_l2(got[b], ref[b]) <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
+
+
+def test_decode_paged_equals_contiguous():
+    """Same rows through a shuffled and an identity block table: bit-identical."""
+    inp = _case(102, [70, 200, 513], 1)
+    outs = []
+    for shuffle in (False, True):
+        cfg, cache, bt, t = decode_setup(inp, shuffle=shuffle, config_id=7)
+        outs.append(run_decode(cfg, cache, t, int(inp.kv_lens.max())).view(torch.int16).cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_decode_deterministic():
+    inp = _case(103, [1000, 3], 2)
+    cfg, cache, bt, t = decode_setup(inp)
+    a = run_decode(cfg, cache, t, int(inp.kv_lens.max())).view(torch.int16).cpu()
+    b = run_decode(cfg, cache, t, int(inp.kv_lens.max())).view(torch.int16).cpu()
+    assert torch.equal(a, b)
+
+
+def test_decode_split_invariance():
+    """A sequence decoded alone or inside a larger batch is cut into different
+    chunks by the device plan; the merged result must agree closely."""
+    big = _case(104, [4000] + [4000] * 63, 1)
+    cfg, cache, bt, t = decode_setup(big)
+    out_big = host(run_decode(cfg, cache, t, 4001))
+    alone = mi.decode_inputs(104, mi.V3, [4000] * 64, 1)
+    # the first sequence alone: same rows and queries
+    one = mi.DecodeInputs(alone.shape, alone.kv_lens[:1], 1, alone.rows[:4001], alone.row_offsets[:1],
+                          alone.q_nope[:1], alone.q_pe[:1], alone.w_uk, alone.w_uv)
+    cfg1, cache1, bt1, t1 = decode_setup(one)
+    out_one = host(run_decode(cfg1, cache1, t1, 4001))
+    assert rel_l2(out_one[0], out_big[0]) <= 5e-3
+
+
+def test_decode_v3_batch64_context4096():
+    """The B=64 x 4096-context decode workload; oracle on sampled (sequence, head) pairs."""
+    ctx = mi.config_context_lens(2)
+    inp = _case(2, ctx, 1)
+    cfg, cache, bt, t = decode_setup(inp, config_id=2)
+    out = run_decode(cfg, cache, t, int(inp.kv_lens.max()))
+    got = host(out)
+    assert np.isfinite(got).all()
+    seqs, heads = [0, 17, 40, 63], [0, 31, 64, 127]
+    ref = oracle_decode(inp, seqs=seqs, heads=heads)
+    err = rel_l2(got[seqs][:, :, heads], ref)
+    print(f"rel_l2(sampled)={err:.3e}")
+    assert err <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0

@@ -1,0 +1,91 @@
+"""Prefill parity (all ten steps: projections, RMSNorm, RoPE, cache append,
+causal absorbed attention, W^UV) against the float64 explicit oracle."""
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_06_amd as mla
+import mla_inputs as mi
+from mla_testutil import BF16_TOL, F32_TOL, config, dev, host, paged_cache, rel_l2
+from oracle import mla_oracle as om
+
+pytestmark = pytest.mark.gpu
+
+WNAMES = ("w_dq", "g_q", "w_uq", "w_qr", "w_dkv", "g_kv", "w_kr", "w_uk", "w_uv")
+
+
+def _prefill(shape, dtype, config_id, B, L, start_pos=0, gain_spread=0.0, shuffle=True, cache=None, w=None,
+             h=None):
+    bf16 = dtype == torch.bfloat16
+    cfg = config(shape, dtype)
+    if w is None:
+        w = mi.weights(config_id, shape, bf16=bf16, gain_spread=gain_spread)
+    if h is None:
+        h = mi.hidden(config_id, shape, B, L, bf16=bf16)
+    if cache is None:
+        kv_end = start_pos + L
+        bt, npages = mi.block_table(config_id, [kv_end] * B, shape.page_size, shuffle=shuffle)
+        cache = paged_cache(cfg, npages, bt)
+    wd = {k: dev(v, dtype) for k, v in w.items()}
+    out = torch.empty((B, L, shape.n_heads, shape.d_head), dtype=dtype, device="cuda")
+    mla.mla_prefill(cfg, cache, wd, dev(h, dtype), out, start_pos=start_pos)
+    torch.cuda.synchronize()
+    return cfg, cache, w, h, out
+
+
+def test_prefill_tiny_fp32_full():
+    """B=1, L=64 tiny layer in fp32 (d=64, n_h=4, d_h=16, d_h^R=8, d_c=32, d_c'=48)."""
+    s = mi.TINY
+    cfg, cache, w, h, out = _prefill(s, torch.float32, 1, 1, 64)
+    ref, rows = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale)
+    got = host(out)[0]
+    err = rel_l2(got, ref)
+    print(f"tiny fp32 rel_l2={err:.3e}")
+    assert err <= F32_TOL
+    # the appended cache rows, read back through the block table
+    bt = cache.block_table.cpu().numpy()
+    pool = host(cache.pool)
+    gathered = om.paged_gather(pool, bt, 0, 64, s.page_size)
+    assert rel_l2(gathered, rows) <= F32_TOL
+    assert int(cache.err_flags.item()) == 0
+
+
+def test_prefill_tiny_fp32_gains_and_batch():
+    """Non-unit RMSNorm gains (pins the gain reading) and two sequences."""
+    s = mi.TINY
+    cfg, cache, w, h, out = _prefill(s, torch.float32, 11, 2, 40, gain_spread=0.5)
+    for b in range(2):
+        ref, _ = om.prefill(h[b], w, s.n_heads, s.rms_eps, s.rope_base, s.scale)
+        assert rel_l2(host(out)[b], ref) <= F32_TOL
+
+
+def test_prefill_chunked_matches_whole_fp32():
+    """Prefill of 64 tokens == prefill of 40 then 24 more at start_pos=40."""
+    s = mi.TINY
+    w = mi.weights(13, s, bf16=False, gain_spread=0.3)
+    h = mi.hidden(13, s, 1, 64, bf16=False)
+    cfg, cache, _, _, out_all = _prefill(s, torch.float32, 13, 1, 64, w=w, h=h)
+    bt, npages = mi.block_table(14, [64], s.page_size, shuffle=True)
+    cache2 = paged_cache(cfg, npages, bt)
+    _prefill(s, torch.float32, 13, 1, 40, w=w, h=h[:, :40], cache=cache2)
+    _, _, _, _, out_tail = _prefill(s, torch.float32, 13, 1, 24, start_pos=40, w=w, h=h[:, 40:], cache=cache2)
+    assert rel_l2(host(out_tail)[0], host(out_all)[0, 40:]) <= F32_TOL
+    ref, _ = om.prefill(h[0, 40:], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, start_pos=40,
+                        past_rows=om.prefill(h[0, :40], w, s.n_heads, s.rms_eps, s.rope_base, s.scale)[1])
+    assert rel_l2(host(out_tail)[0], ref) <= F32_TOL
+
+
+def test_prefill_v3_small_bf16_full():
+    """DeepSeek-V3 shapes, B=2, L=96 (several 32-key tiles and a ragged tail)."""
+    s = mi.V3
+    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 31, 2, 96)
+    got = host(out)
+    assert np.isfinite(got).all()
+    for b in range(2):
+        ref, rows = om.prefill(h[b], w, s.n_heads, s.rms_eps, s.rope_base, s.scale)
+        err = rel_l2(got[b], ref)
+        print(f"b={b} rel_l2={err:.3e}")
+        assert err <= BF16_TOL
+        gathered = om.paged_gather(host(cache.pool), cache.block_table.cpu().numpy(), b, 96, s.page_size)
+        assert rel_l2(gathered, rows) <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
