@@ -1,0 +1,234 @@
+"""Throughput of the MLA hot path on one MI355X.
+
+Headline (one JSON line on stdout): decode of 64 sequences x 4096 cached
+tokens + 1 new token each, DeepSeek-V3 MLA heads (n_h = 128, d_c = 512,
+d_h^R = 64, 576 bf16 values cached per token, 64-token pages with a shuffled
+block table).  A step is one mla_decode call: absorption of W^UK into the
+queries, the split-context latent attention, the merge and W^UV.  `value` is
+latent-cache bytes per second (the cache is read once per step; 302,063,616 B).
+
+Also measured and reported in the same line:
+  * roofline of the dominant kernel (the latent-attention kernel), timed with
+    HIP events recorded around that kernel alone on its launch stream;
+  * the causal prefill workload (B = 1, L = 8192, d = 7168, all projections,
+    cache append and attention) in TFLOP/s, with its attention kernel's roofline;
+  * the float64 oracle on the host cores for a bounded sample (cpu_baseline).
+
+Inputs are seeded synthetic tensors (mla_inputs), resident in HBM before the
+timed region.  Four copies of the 302 MB cache are rotated so the 256 MB
+last-level cache cannot serve a step from the previous one.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import head_latent_attention_06_amd as mla  # noqa: E402
+import mla_inputs as mi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MLA decode latent-KV GB/s + prefill TFLOP/s, % of MI355X roofline"
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (the library records them on its launch stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e)
+
+    def pair(self, i):
+        return self.ev[2 * i], self.ev[2 * i + 1]
+
+    def elapsed_ms(self, i) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[2 * i], self.ev[2 * i + 1]) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def _up(a, dtype=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(dtype)
+
+
+def decode_workload(copies: int):
+    inp = mi.decode_inputs(2, mi.V3, mi.config_context_lens(2), 1)
+    cfg = mla.Config()
+    bt, npages = mi.block_table(2, inp.kv_lens, cfg.page_size, shuffle=True)
+    pool = torch.empty((npages, cfg.page_size, cfg.row), dtype=torch.bfloat16, device="cuda")
+    flat = pool.view(-1, cfg.row)
+    for b in range(len(inp.kv_lens)):
+        n = int(inp.kv_lens[b])
+        pos = np.arange(n)
+        idx = torch.from_numpy(bt[b, pos // cfg.page_size].astype(np.int64) * cfg.page_size + pos % cfg.page_size)
+        flat[idx.cuda()] = _up(inp.seq_rows(b))
+    btd = torch.from_numpy(bt).cuda()
+    caches = [mla.PagedCache(pool if i == 0 else pool.clone(), btd) for i in range(copies)]
+    t = dict(q_nope=_up(inp.q_nope), q_pe=_up(inp.q_pe), w_uk=_up(inp.w_uk), w_uv=_up(inp.w_uv),
+             kv_lens=torch.from_numpy(inp.kv_lens).cuda())
+    return inp, cfg, caches, t
+
+
+def run_decode_bench(steps: int, warmup: int):
+    inp, cfg, caches, t = decode_workload(4)
+    B, max_kv = len(inp.kv_lens), int(inp.kv_lens.max())
+    out = torch.empty((B, 1, cfg.n_heads, cfg.d_head), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_size(cfg, B, 1, max_kv), dtype=torch.uint8, device="cuda")
+    ev = HipEvents(steps)
+
+    def step(i, evs=None):
+        mla.mla_decode(cfg, caches[i % len(caches)], t["kv_lens"], max_kv, t["q_nope"], t["q_pe"], t["w_uk"],
+                       t["w_uv"], out, ws=ws, attn_events=evs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, ev.pair(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    latent_bytes = int(inp.kv_lens.sum()) * cfg.row * 2
+    flops = int(inp.kv_lens.sum()) * cfg.n_heads * (cfg.row + cfg.d_c) * 2
+    return dict(inp=inp, wall=wall, attn_ms=attn_ms, latent_bytes=latent_bytes, attn_flops=flops)
+
+
+def prefill_flops(s: mi.Shape, L: int) -> dict:
+    T = L
+    pairs = L * (L + 1) // 2
+    H, dh, dr, dc, dcq, d = s.n_heads, s.d_head, s.d_rope, s.d_c, s.d_cq, s.d_model
+    f = {
+        "kv_down_proj": 2 * T * (dc + dr) * d,
+        "q_down_proj": 2 * T * dcq * d,
+        "q_up_proj": 2 * T * H * dh * dcq,
+        "q_rope_proj": 2 * T * H * dr * dcq,
+        "absorb_w_uk": 2 * T * H * dh * dc,
+        "attention": 2 * pairs * H * (dc + dr + dc),
+        "w_uv": 2 * T * H * dc * dh,
+    }
+    f["total"] = sum(f.values())
+    # explicit-form attention (k, v materialised per head, d_qk = 192, d_v = 128)
+    f["explicit_equivalent_total"] = f["total"] - f["attention"] - f["absorb_w_uk"] + 2 * pairs * H * (dh + dr + dh) \
+        + 2 * T * H * dh * dc * 2
+    return f
+
+
+def run_prefill_bench(steps: int, warmup: int, L: int = 8192):
+    s = mi.V3
+    cfg = mla.Config()
+    w = {k: _up(v) for k, v in mi.weights(3, s).items()}
+    h = _up(mi.hidden(3, s, 1, L))
+    bt, npages = mi.block_table(3, [L], s.page_size, shuffle=True)
+    cache = mla.PagedCache(torch.zeros((npages, s.page_size, cfg.row), dtype=torch.bfloat16, device="cuda"),
+                           torch.from_numpy(bt).cuda())
+    out = torch.empty((1, L, s.n_heads, s.d_head), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_prefill_workspace_size(cfg, 1, L), dtype=torch.uint8, device="cuda")
+    ev = HipEvents(steps)
+    for _ in range(warmup):
+        mla.mla_prefill(cfg, cache, w, h, out, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        mla.mla_prefill(cfg, cache, w, h, out, ws=ws, attn_events=ev.pair(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    return dict(wall=wall, attn_ms=attn_ms, flops=prefill_flops(s, L), L=L)
+
+
+def cpu_baseline(inp, heads: int):
+    """The float64 oracle on sequence 0, `heads` of the 128 heads, all 4097 keys."""
+    from oracle import mla_oracle as om
+    s = inp.shape
+    rows = [inp.seq_rows(0)]
+    t0 = time.perf_counter()
+    om.decode(rows, inp.kv_lens[:1], 1, inp.q_nope[:1], inp.q_pe[:1], inp.w_uk, inp.w_uv, s.d_c, s.scale,
+              heads=list(range(heads)))
+    dt = time.perf_counter() - t0
+    # the sample is heads/128 of one sequence's step: that share of its latent rows
+    eq_bytes = int(inp.kv_lens[0]) * s.row * 2 * heads / s.n_heads
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    return dict(value=eq_bytes / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"float64 explicit MLA (numpy, {threads} BLAS threads), sequence 0 of the decode workload, "
+                       f"heads 0..{heads - 1} of 128 over all {int(inp.kv_lens[0])} cached rows, {dt:.1f} s; "
+                       f"scaled by the share of the latent rows it covers")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
+              "build: sequences shard across GPUs with no exchange (see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    d = run_decode_bench(args.steps, args.warmup)
+    ms = d["wall"] / args.steps * 1e3
+    value = d["latent_bytes"] / (ms * 1e-3) / 1e9
+    attn_gbs = d["latent_bytes"] / (d["attn_ms"] * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "MLA decode step, B=64 sequences x (4096 cached + 1 new) tokens, s_q=1, "
+                               "n_h=128, d_h=128, d_c=512, d_h^R=64, 64-token pages, shuffled block table",
+                   "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel", "kernel_ms": round(d["attn_ms"], 5),
+                     "algorithmic_bytes": d["latent_bytes"],
+                     "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
+    }
+    if not args.no_prefill:
+        p = run_prefill_bench(max(2, args.steps // 4), max(1, args.warmup // 2))
+        pms = p["wall"] / max(2, args.steps // 4) * 1e3
+        f = p["flops"]
+        res["prefill"] = {
+            "workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention",
+            "ms_per_step": round(pms, 3), "tflops_executed": round(f["total"] / (pms * 1e-3) / 1e12, 1),
+            "tokens_per_s": round(p["L"] / (pms * 1e-3), 1),
+            "explicit_equivalent_tflops": round(f["explicit_equivalent_total"] / (pms * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "kernel_ms": round(p["attn_ms"], 4),
+                         "achieved": round(f["attention"] / (p["attn_ms"] * 1e-3) / 1e12, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(f["attention"] / (p["attn_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d["inp"], args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

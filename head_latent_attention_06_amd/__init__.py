@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "mla_decode_workspace_size": (I32, [CP, I32, I32, I32, ctypes.POINTER(SZ)]),
             "mla_decode": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
             "mla_decode_num_splits": (I32, [CP, I32, I32, I32]),
+            "mla_decode_profiled": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P, P, P]),
+            "mla_prefill_profiled": (I32, [CP, KP, WP, P, I32, I32, I32, P, P, SZ, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -178,14 +180,18 @@ def mla_prefill_workspace_size(cfg: Config, B: int, L: int, start_pos: int = 0) 
 
 
 def mla_prefill(cfg: Config, cache: PagedCache, weights: dict, h, out, start_pos: int = 0, ws=None,
-                stream=None) -> None:
-    """Causal prefill of h [B, L, d_model] into out [B, L, n_heads, d_head]."""
+                stream=None, attn_events=None) -> None:
+    """Causal prefill of h [B, L, d_model] into out [B, L, n_heads, d_head].
+
+    attn_events: optional (start, stop) raw hipEvent_t handles recorded around
+    the attention kernel (mla_prefill_profiled)."""
     B, L = h.shape[0], h.shape[1]
     if ws is None:
         ws = _workspace(mla_prefill_workspace_size(cfg, B, L, start_pos), h.device)
-    _check(lib().mla_prefill(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), ctypes.byref(_weights(weights)),
-                             _ptr(h), B, L, start_pos, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
-           "mla_prefill")
+    ev0, ev1 = attn_events if attn_events is not None else (None, None)
+    _check(lib().mla_prefill_profiled(ctypes.byref(cfg._c()), ctypes.byref(cache._c()),
+                                      ctypes.byref(_weights(weights)), _ptr(h), B, L, start_pos, _ptr(out), _ptr(ws),
+                                      ws.numel(), _stream(stream), ev0, ev1), "mla_prefill")
 
 
 def mla_decode_workspace_size(cfg: Config, B: int, s_q: int, max_kv_len: int) -> int:
@@ -200,11 +206,15 @@ def mla_decode_num_splits(cfg: Config, B: int, s_q: int, max_kv_len: int) -> int
 
 
 def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope, q_pe, w_uk, w_uv, out, ws=None,
-               stream=None) -> None:
-    """One decode step: q_nope [B, s_q, H, d_head], q_pe [B, s_q, H, d_rope] -> out [B, s_q, H, d_head]."""
+               stream=None, attn_events=None) -> None:
+    """One decode step: q_nope [B, s_q, H, d_head], q_pe [B, s_q, H, d_rope] -> out [B, s_q, H, d_head].
+
+    attn_events: optional (start, stop) raw hipEvent_t handles recorded around
+    the attention kernel (mla_decode_profiled)."""
     B, s_q = q_nope.shape[0], q_nope.shape[1]
     if ws is None:
         ws = _workspace(mla_decode_workspace_size(cfg, B, s_q, max_kv_len), q_nope.device)
-    _check(lib().mla_decode(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens), int(max_kv_len), B,
-                            s_q, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(ws), ws.numel(),
-                            _stream(stream)), "mla_decode")
+    ev0, ev1 = attn_events if attn_events is not None else (None, None)
+    _check(lib().mla_decode_profiled(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens),
+                                     int(max_kv_len), B, s_q, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream), ev0, ev1), "mla_decode")

@@ -76,9 +76,9 @@ int64_t max_plan_items(const mla_config* c, int64_t n_rows, int32_t max_kv, int3
 
 // ----- workspace layouts --------------------------------------------------
 struct DecodeWs {
-  void *q_abs, *o_lat;
+  void *q_lat, *o_lat, *part_o;
   int32_t* plan;
-  float *part_acc, *part_ml;
+  float* part_ml;
   int64_t max_items;
 };
 
@@ -88,21 +88,22 @@ DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, i
   DecodeWs d{};
   const int64_t rows = (int64_t)B * s_q, H = c->n_heads, row = c->d_c + c->d_rope;
   const size_t e = bf16 ? 2 : 4;
-  d.q_abs = cv.take(rows * H * row * e);
+  d.q_lat = cv.take(rows * H * c->d_c * e);
   d.o_lat = cv.take(rows * H * c->d_c * e);
   if (bf16) {
     d.max_items = max_plan_items(c, rows, max_kv, DECODE_TARGET_ITEMS);
     d.plan = (int32_t*)cv.take((rows + 3) * 4);
-    d.part_acc = (float*)cv.take(d.max_items * H * c->d_c * 4);
+    d.part_o = cv.take(d.max_items * H * c->d_c * 2);
     d.part_ml = (float*)cv.take(d.max_items * H * 2 * 4);
   }
+  (void)row;
   *total = cv.off;
   return d;
 }
 
 struct PrefillWs {
-  float *kv_raw, *cq_raw, *qr_raw, *rope_cs, *part_acc, *part_ml;
-  void *cq, *qc, *q_abs, *o_lat;
+  float *kv_raw, *cq_raw, *qr_raw, *rope_cs, *part_ml;
+  void *cq, *qc, *q_abs, *o_lat, *part_o;
   int32_t* plan;
   int64_t max_items;
   bool split;
@@ -128,7 +129,7 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, i
     p.max_items = max_plan_items(c, T, kv_end, 0);
     p.plan = (int32_t*)cv.take((T + 3) * 4);
     if (p.split) {
-      p.part_acc = (float*)cv.take(p.max_items * H * c->d_c * 4);
+      p.part_o = cv.take(p.max_items * H * c->d_c * 2);
       p.part_ml = (float*)cv.take(p.max_items * H * 2 * 4);
     }
   }
@@ -197,10 +198,13 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   return MLA_OK;
 }
 
-AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_abs, const int32_t* kv_lens,
-                   int32_t uniform_kv, int32_t max_kv, int32_t B, int32_t s_q) {
+AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_lat, int32_t ld_q, const void* q_rope,
+                   int32_t ld_r, const int32_t* kv_lens, int32_t uniform_kv, int32_t max_kv, int32_t B, int32_t s_q) {
   AttnArgs a{};
-  a.q_abs = q_abs;
+  a.q_lat = q_lat;
+  a.ld_q = ld_q;
+  a.q_rope = q_rope;
+  a.ld_r = ld_r;
   a.pool = k->pool;
   a.block_table = k->block_table;
   a.num_pages = k->num_pages;
@@ -221,20 +225,24 @@ AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_abs
 
 // Attention + merge + W^UV for rows whose absorbed queries are in q_abs.
 mla_status attend(const mla_config* c, bool bf16, AttnArgs a, int32_t* plan, int64_t max_items, int32_t target,
-                  bool need_merge, float* part_acc, float* part_ml, void* o_lat, const void* w_uv, void* out,
-                  hipStream_t st) {
+                  bool need_merge, void* part_o, float* part_ml, void* o_lat, const void* w_uv, void* out,
+                  hipStream_t st, void* ev0, void* ev1) {
   const int64_t rows = (int64_t)a.B * a.s_q;
   a.o_lat = o_lat;
   if (bf16) {
     a.plan = plan;
     a.max_items = (int32_t)max_items;
-    a.part_acc = part_acc;
+    a.part_o = part_o;
     a.part_ml = part_ml;
     MLA_HIP(launch_attn_plan(a, plan, target, MIN_CHUNK, max_chunk_keys(c) / 32 * 32, st));
+    if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
     MLA_HIP(launch_attn_bf16(a, st));
+    if (ev1) MLA_HIP(hipEventRecord((hipEvent_t)ev1, st));
     if (need_merge) MLA_HIP(launch_merge_bf16(a, st));
   } else {
+    if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
     MLA_HIP(launch_attn_f32(a, st));
+    if (ev1) MLA_HIP(hipEventRecord((hipEvent_t)ev1, st));
   }
   // o[t, i, :] = W_i^UV o_lat[t, i, :]
   GemmArgs g = gemm(o_lat, (int64_t)c->n_heads * c->d_c, c->d_c, w_uv, c->d_c, (int64_t)c->d_head * c->d_c, out,
@@ -326,6 +334,12 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t 
 
 mla_status mla_prefill(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w, const void* h,
                        int32_t B, int32_t L, int32_t start_pos, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return mla_prefill_profiled(cfg, cache, w, h, B, L, start_pos, out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
+                                const void* h, int32_t B, int32_t L, int32_t start_pos, void* out, void* ws,
+                                size_t ws_bytes, void* stream, void* attn_start, void* attn_stop) {
   bool bf16;
   mla_status s = check_cfg(cfg, &bf16);
   if (s != MLA_OK) return s;
@@ -368,9 +382,12 @@ mla_status mla_prefill(const mla_config* cfg, const mla_kv_cache* cache, const m
                                   cfg->d_head, H, true, bf16), st)) != MLA_OK)
     return s;
   // step (10) in absorbed form over rows [0, start_pos + t]
-  AttnArgs a = attn_args(cfg, cache, p.q_abs, nullptr, (int32_t)kv_end, (int32_t)kv_end, B, L);
+  const size_t e = bf16 ? 2 : 4;
+  AttnArgs a = attn_args(cfg, cache, p.q_abs, row, (const unsigned char*)p.q_abs + cfg->d_c * e, row, nullptr,
+                         (int32_t)kv_end, (int32_t)kv_end, B, L);
   a.longest_first = 1;
-  return attend(cfg, bf16, a, p.plan, p.max_items, 0, p.split, p.part_acc, p.part_ml, p.o_lat, w->w_uv, out, st);
+  return attend(cfg, bf16, a, p.plan, p.max_items, 0, p.split, p.part_o, p.part_ml, p.o_lat, w->w_uv, out, st,
+                attn_start, attn_stop);
 }
 
 mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t s_q, int32_t max_kv_len,
@@ -393,6 +410,14 @@ int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t s_q, int
 mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens, int32_t max_kv_len,
                       int32_t B, int32_t s_q, const void* q_nope, const void* q_pe, const void* w_uk,
                       const void* w_uv, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return mla_decode_profiled(cfg, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, ws, ws_bytes,
+                             stream, nullptr, nullptr);
+}
+
+mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                               int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, void* out, void* ws, size_t ws_bytes,
+                               void* stream, void* attn_start, void* attn_stop) {
   bool bf16;
   mla_status s = check_cfg(cfg, &bf16);
   if (s != MLA_OK) return s;
@@ -411,17 +436,16 @@ mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const in
   DecodeWs d = decode_layout(cfg, bf16, B, s_q, max_kv_len, ws, &need);
   if (need > ws_bytes) return MLA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int rows = B * s_q, H = cfg->n_heads, row = cfg->d_c + cfg->d_rope;
-  // absorption: Q_abs[t, i, :d_c] = W_i^UK^T q^C[t, i]; Q_abs[t, i, d_c:] = q^R[t, i]
+  const int rows = B * s_q, H = cfg->n_heads;
+  // absorption: q_lat[t, i, :] = W_i^UK^T q^C[t, i]  (q^R is read from q_pe directly)
   if ((s = launch_gemm(bf16, gemm(q_nope, (int64_t)H * cfg->d_head, cfg->d_head, w_uk, cfg->d_c,
-                                  (int64_t)cfg->d_head * cfg->d_c, d.q_abs, (int64_t)H * row, row, rows, cfg->d_c,
-                                  cfg->d_head, H, true, bf16), st)) != MLA_OK)
+                                  (int64_t)cfg->d_head * cfg->d_c, d.q_lat, (int64_t)H * cfg->d_c, cfg->d_c, rows,
+                                  cfg->d_c, cfg->d_head, H, true, bf16), st)) != MLA_OK)
     return s;
-  MLA_HIP(launch_copy_heads(q_pe, d.q_abs, row, cfg->d_c, rows, H, cfg->d_rope, bf16 ? 2 : 4, st));
-  AttnArgs a = attn_args(cfg, cache, d.q_abs, kv_lens, 0, max_kv_len, B, s_q);
+  AttnArgs a = attn_args(cfg, cache, d.q_lat, cfg->d_c, q_pe, cfg->d_rope, kv_lens, 0, max_kv_len, B, s_q);
   a.longest_first = 0;
-  return attend(cfg, bf16, a, d.plan, d.max_items, DECODE_TARGET_ITEMS, true, d.part_acc, d.part_ml, d.o_lat, w_uv,
-                out, st);
+  return attend(cfg, bf16, a, d.plan, d.max_items, DECODE_TARGET_ITEMS, true, d.part_o, d.part_ml, d.o_lat, w_uv,
+                out, st, attn_start, attn_stop);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@
 //  * V^T is built while staging: each thread loads 8 keys x 8 dims, transposes
 //    them in registers and writes 16-byte rows of a [dim][key] LDS tile whose
 //    key order matches the MFMA k-slot order of P^T.  Row permutation
-//    dim ^ ((dim >> 3) & 7) with an 80-byte stride keeps both the transposed
+//    dim ^ ((dim >> 3) & 15) with an 80-byte stride keeps both the transposed
 //    writes and the MFMA operand reads free of bank conflicts.
 //  * Online softmax in the log2 domain; the running max is only raised when
 //    a tile's max exceeds it by more than 8 (p <= 256 stays exact in fp32),
@@ -92,11 +92,11 @@ void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int n_items = a.plan[0];
   const int chunk = a.plan[1];
-  // Consecutive logical blocks (head groups of one item, chunks of one row,
-  // rows of one sequence) share an XCD and its L2; with longest_first the
-  // items run in reverse plan order instead (rows with most keys come last).
-  const int lb = a.longest_first ? (int)blockIdx.x : xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int bid = lb / n_hg, hg = lb % n_hg;
+  // The grid is an upper bound on the plan's items, so blocks map to items in
+  // launch order: the real items are then spread round-robin over all XCDs.
+  // With longest_first they run in reverse plan order (rows with most keys are
+  // planned last).
+  const int bid = (int)blockIdx.x / n_hg, hg = (int)blockIdx.x % n_hg;
   if (bid >= n_items) return;
   const int w = a.longest_first ? n_items - 1 - bid : bid;
   const int n_rows = a.B * a.s_q;
@@ -125,16 +125,19 @@ void attn_bf16_kernel(AttnArgs a) {
   const int64_t qrow = row;
   const float scale_log2 = a.scale * LOG2E;
 
-  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15.
-  // Heads past H load as zero (outside the buffer resource).
+  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
+  // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
   u32x4 qf[36];
   {
     const int nh = wave_on ? min(32, a.H - head0) : 0;
-    const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc((const bf16*)a.q_abs + (qrow * a.H + (wave_on ? head0 : 0)) * ROW, nh * ROW * 2);
-    const int qo = l32 * ROW * 2 + 16 * hi;
+    const int64_t hrow = qrow * a.H + (wave_on ? head0 : 0);
+    const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
+    const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
 #pragma unroll
-    for (int j = 0; j < 36; ++j) qf[j] = buf_ld16(qr, qo + 32 * j);
+    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
+#pragma unroll
+    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
   }
 
   f32x16 acc[16];
@@ -151,14 +154,21 @@ void attn_bf16_kernel(AttnArgs a) {
   const int rope_off = (tid >> 3) * ROW * 2 + DC * 2 + 16 * (tid & 7);
   unsigned char* const kw0 = smem + (16 * (wave >> 1) + 4 * (wave & 1)) * KSTR + 16 * lane;
   unsigned char* const rw0 = smem + (tid >> 3) * KSTR + DC * 2 + 16 * (tid & 7);
-  // V^T layout: dim row d at d * VSTR, key slot group q at ((q ^ ((d >> 3) & 3)) * 16).
-  // A staging write covers dims 8*lane + 0..7 of one slot group, an MFMA read 32
-  // consecutive dims of one group, so each side needs a single base address.
-  unsigned char* const vw0 = smem + KBYTES + 8 * lane * VSTR + ((wave ^ (lane & 3)) * 16);
+  // V^T layout: dim d lives in physical row vrow(d) = d ^ ((d >> 3) & 15) (80-byte
+  // rows), key slot group q at q * 16 bytes.  Both the staging writes (lanes
+  // cover dims 8*lane + j) and the MFMA reads (32 consecutive dims) are then
+  // free of bank conflicts with 16-lane phases over 64 banks and with 8-lane
+  // phases over 32 banks.  For dims 8*lane + j the row is
+  // wrow + (j ^ (lane & 7)) with wrow = 16*(lane/2) + 8*((lane ^ (lane >> 3)) & 1).
+  const int wrow = 16 * (lane >> 1) + 8 * ((lane ^ (lane >> 3)) & 1);
+  const int wl3 = lane & 7;
+  unsigned char* const vw0 = smem + KBYTES + wave * 16;
   const unsigned char* const kr0 = smem + l32 * KSTR + hi * 16;
-  const int y = l32 >> 3;  // (dim >> 3) & 3 for dim = 32*blk + l32
-  const unsigned char* const vr0 = smem + KBYTES + l32 * VSTR + (((0 + hi) ^ y) * 16);
-  const unsigned char* const vr1 = smem + KBYTES + l32 * VSTR + (((2 + hi) ^ y) * 16);
+  // reads: dim 32*blk + l32 -> row 32*blk + (l32 ^ ((4*(blk & 3) + (l32 >> 3)) & 15))
+  const unsigned char* vr[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    vr[b] = smem + KBYTES + (l32 ^ ((4 * b + (l32 >> 3)) & 15)) * VSTR + hi * 16;
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   u32x4 sv[8], sr;
@@ -196,8 +206,8 @@ void attn_bf16_kernel(AttnArgs a) {
         o0_[r2] = (x0_ & 0xFFFFu) | (x1_ << 16);                                                  \
         o1_[r2] = (x0_ >> 16) | (x1_ & 0xFFFF0000u);                                              \
       }                                                                                           \
-      st16(vw0 + off_ + (2 * c2) * VSTR, o0_);                                                    \
-      st16(vw0 + off_ + (2 * c2 + 1) * VSTR, o1_);                                                \
+      st16(vw0 + off_ + (wrow + ((2 * c2) ^ wl3)) * VSTR, o0_);                                   \
+      st16(vw0 + off_ + (wrow + ((2 * c2 + 1) ^ wl3)) * VSTR, o1_);                               \
     }                                                                                             \
   }
 
@@ -245,7 +255,7 @@ void attn_bf16_kernel(AttnArgs a) {
       constexpr int VW = 3;  // V fragments in flight
       u32x4 vf[VW];
 #pragma unroll
-      for (int i = 0; i < VW - 1; ++i) vf[i] = *(const u32x4*)(vr0 + off + i * 32 * VSTR);
+      for (int i = 0; i < VW - 1; ++i) vf[i] = *(const u32x4*)(vr[i & 3] + off + i * 32 * VSTR);
       __builtin_amdgcn_sched_barrier(0);
       // ---- online softmax (log2 domain); lane holds keys kb + 8*(i/4) + 4*hi + i%4 of head l32
       float mloc = -INFINITY;
@@ -294,7 +304,7 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int m = 0; m < 32; ++m) {  // k step q = m/16, dim block m%16
         if (m + VW - 1 < 32) {
           const int mn = m + VW - 1;
-          vf[mn % VW] = *(const u32x4*)(((mn >> 4) ? vr1 : vr0) + off + (mn & 15) * 32 * VSTR);
+          vf[mn % VW] = *(const u32x4*)(vr[mn & 3] + off + (mn & 15) * 32 * VSTR + (mn >> 4) * 32);
         }
         if (m == 0) {
           asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0]) : "v"(vf[0]), "v"(pf[0]));
@@ -322,37 +332,29 @@ void attn_bf16_kernel(AttnArgs a) {
   const float l_tot = pair_sum32(l_run);
   const int head = head0 + l32;
   if (head >= a.H) return;
-  if (n_split_row == 1) {
-    const float inv = 1.f / l_tot;
-    bf16* o = (bf16*)a.o_lat + (qrow * a.H + head) * DC + 4 * hi;
+  // normalised by this chunk's sum: the final output when the row is one
+  // chunk, else a partial the merge combines with weights 2^(m - m*) * l
+  const float inv = 1.f / l_tot;
+  bf16* o = (n_split_row == 1 ? (bf16*)a.o_lat + (qrow * a.H + head) * DC
+                              : (bf16*)a.part_o + ((int64_t)w * a.H + head) * DC) + 4 * hi;
 #pragma unroll
-    for (int blk = 0; blk < 16; ++blk)
+  for (int blk = 0; blk < 16; ++blk)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 v;
-        v[0] = pack_bf16x2(acc[blk][4 * q4] * inv, acc[blk][4 * q4 + 1] * inv);
-        v[1] = pack_bf16x2(acc[blk][4 * q4 + 2] * inv, acc[blk][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(o + 32 * blk + 8 * q4) = v;
-      }
-  } else {
-    const int64_t slot = (int64_t)w * a.H + head;
-    float* pa = a.part_acc + slot * DC + 4 * hi;
-#pragma unroll
-    for (int blk = 0; blk < 16; ++blk)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v = {acc[blk][4 * q4], acc[blk][4 * q4 + 1], acc[blk][4 * q4 + 2], acc[blk][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(pa + 32 * blk + 8 * q4) = v;
-      }
-    if (hi == 0) {
-      a.part_ml[slot * 2] = m_run;
-      a.part_ml[slot * 2 + 1] = l_tot;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 v;
+      v[0] = pack_bf16x2(acc[blk][4 * q4] * inv, acc[blk][4 * q4 + 1] * inv);
+      v[1] = pack_bf16x2(acc[blk][4 * q4 + 2] * inv, acc[blk][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(o + 32 * blk + 8 * q4) = v;
     }
+  if (n_split_row > 1 && hi == 0) {
+    const int64_t slot = (int64_t)w * a.H + head;
+    a.part_ml[slot * 2] = m_run;
+    a.part_ml[slot * 2 + 1] = l_tot;
   }
 }
 
-// Merge of split partials (m_k in the log2 domain):
-//   o_lat = sum_k 2^(m_k - m*) acc_k / sum_k 2^(m_k - m*) l_k,  m* = max_k m_k.
+// Merge of split partials o_k = acc_k / l_k (m_k in the log2 domain):
+//   o_lat = sum_k 2^(m_k - m*) l_k o_k / sum_k 2^(m_k - m*) l_k,  m* = max_k m_k.
 // Rows cut into a single chunk were written by the attention kernel; rows
 // with no chunk (invalid length) are written as zero.
 __global__ __launch_bounds__(128) void merge_bf16_kernel(AttnArgs a) {
@@ -371,10 +373,13 @@ __global__ __launch_bounds__(128) void merge_bf16_kernel(AttnArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < n; ++k) {
       const int64_t slot = (int64_t)(i0 + k) * a.H + head;
-      const float wk = exp2f(a.part_ml[slot * 2] - mstar);
-      L += wk * a.part_ml[slot * 2 + 1];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_acc + slot * DC + 4 * t);
-      acc += wk * v;
+      const float wk = exp2f(a.part_ml[slot * 2] - mstar) * a.part_ml[slot * 2 + 1];
+      L += wk;
+      const u32x2 v = *reinterpret_cast<const u32x2*>((const bf16*)a.part_o + slot * DC + 4 * t);
+      acc[0] += wk * bf16_lo(v[0]);
+      acc[1] += wk * bf16_hi(v[0]);
+      acc[2] += wk * bf16_lo(v[1]);
+      acc[3] += wk * bf16_hi(v[1]);
     }
     const float inv = 1.f / L;
     outv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -482,8 +487,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     return;
   }
   const int kend = kv - a.s_q + s + 1;
-  const float* q = (const float*)a.q_abs + (qrow * a.H + head) * row;
-  for (int i = tid; i < row; i += 256) qs[i] = q[i];
+  const float* ql = (const float*)a.q_lat + (qrow * a.H + head) * a.ld_q;
+  const float* qr = (const float*)a.q_rope + (qrow * a.H + head) * a.ld_r;
+  for (int i = tid; i < a.d_c; i += 256) qs[i] = ql[i];
+  for (int i = tid; i < a.d_rope; i += 256) qs[a.d_c + i] = qr[i];
   const float* pool = (const float*)a.pool;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};

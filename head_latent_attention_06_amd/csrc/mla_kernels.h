@@ -14,7 +14,9 @@ namespace mla {
 // Plan layout (int32, device): [0] n_items, [1] chunk, [2 + r] first item of
 // row r for r = 0 .. n_rows (row r owns items plan[2+r] .. plan[3+r]-1).
 struct AttnArgs {
-  const void* q_abs;          // [n_rows, H, d_c + d_rope]: [W_i^UK^T q^C ; q^R]
+  const void* q_lat;          // [n_rows, H, ld_q]: first d_c = W_i^UK^T q^C_i
+  const void* q_rope;         // [n_rows, H, ld_r]: first d_rope = q^R_i (rotated)
+  int32_t ld_q, ld_r;
   const void* pool;           // [num_pages, page_size, d_c + d_rope]
   const int32_t* block_table; // [B, max_pages]
   int64_t num_pages;
@@ -28,8 +30,8 @@ struct AttnArgs {
   int32_t max_items;          // grid size (upper bound on plan[0])
   int32_t longest_first;      // run items in reverse order (rows with most keys last in the plan)
   float scale;                // softmax scale
-  float* part_acc;            // [max_items, H, d_c]  rows split into several chunks
-  float* part_ml;             // [max_items, H, 2]
+  void* part_o;               // [max_items, H, d_c] bf16: chunk output / chunk sum
+  float* part_ml;             // [max_items, H, 2]: chunk max (log2 domain), chunk sum
   void* o_lat;                // [n_rows, H, d_c]
 };
 
@@ -93,9 +95,5 @@ hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out,
 hipError_t launch_rope_heads(const float* x, const float* cs, int32_t table_rows, void* out,
                              int64_t ld_out, int32_t out_off, int32_t T, int32_t H, int32_t d_rope,
                              int32_t bf16_out, hipStream_t st);
-
-// Copy per-head rows src [T, H, w] into dst[t, h, dst_off ...] (row stride ld_dst).
-hipError_t launch_copy_heads(const void* src, void* dst, int64_t ld_dst, int32_t dst_off, int32_t T,
-                             int32_t H, int32_t w, int32_t elem_bytes, hipStream_t st);
 
 }  // namespace mla

@@ -1,5 +1,5 @@
 // Element-wise parts of the MLA layer: the cache append (RMSNorm of c^KV,
-// RoPE of k^R, paged scatter), the RMSNorm of c^Q, RoPE of q^R and packing.
+// RoPE of k^R, paged scatter), the RMSNorm of c^Q and RoPE of q^R.
 //
 // Definitions (notes page "【论文解读】DeepSeek-V3"):
 //  * RMSNorm after each compressed latent (section 二(二)1):
@@ -137,16 +137,6 @@ __global__ void rope_heads_kernel(const float* x, const float* cs, int table_row
   o[2 * p + 1] = from_f32<TOUT>(c[1] * x0 + c[0] * x1);
 }
 
-// One thread per 4-byte word of a head row.
-__global__ void copy_heads_kernel(const uint32_t* src, unsigned char* dst, int64_t ld_dst_bytes, int dst_off_bytes,
-                                  int64_t rows, int words) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * words) return;
-  const int64_t r = idx / words;
-  const int wd = (int)(idx % words);
-  *(uint32_t*)(dst + r * ld_dst_bytes + dst_off_bytes + 4 * wd) = src[idx];
-}
-
 unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -192,16 +182,6 @@ hipError_t launch_rope_heads(const float* x, const float* cs, int32_t table_rows
   else
     hipLaunchKernelGGL((rope_heads_kernel<float>), dim3(blocks_for(n, 256)), dim3(256), 0, st, x, cs, table_rows,
                        (float*)out, ld_out, out_off, (int64_t)T, H, d_rope);
-  return hipGetLastError();
-}
-
-hipError_t launch_copy_heads(const void* src, void* dst, int64_t ld_dst, int32_t dst_off, int32_t T, int32_t H,
-                             int32_t w, int32_t elem_bytes, hipStream_t st) {
-  const int64_t rows = (int64_t)T * H;
-  const int words = w * elem_bytes / 4;
-  if (rows <= 0 || words <= 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_heads_kernel, dim3(blocks_for(rows * words, 256)), dim3(256), 0, st, (const uint32_t*)src,
-                     (unsigned char*)dst, ld_dst * elem_bytes, dst_off * elem_bytes, rows, words);
   return hipGetLastError();
 }
 

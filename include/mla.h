@@ -169,6 +169,18 @@ mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const in
                       const void* q_pe, const void* w_uk, const void* w_uv, void* out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Measurement variants: identical to mla_decode / mla_prefill, and in
+ * addition record attn_start and attn_stop (hipEvent_t, either may be NULL) on
+ * `stream` immediately before and after the latent-attention kernel, so a
+ * caller can time that kernel alone with hipEventElapsedTime. */
+mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                               int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, void* out, void* ws, size_t ws_bytes,
+                               void* stream, void* attn_start, void* attn_stop);
+mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
+                                const void* h, int32_t B, int32_t L, int32_t start_pos, void* out, void* ws,
+                                size_t ws_bytes, void* stream, void* attn_start, void* attn_stop);
+
 /* Upper bound on the attention work items (split partial slots) mla_decode
  * plans for these sizes; the device plan cuts each query row's visible keys
  * into chunks from the actual kv_lens.  Host helper for tests and sizing;

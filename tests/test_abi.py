@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, and rejects bad arguments on the host before any
+launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_06_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+FAKE = 0x7000_0000_0000  # an aligned non-null address; nothing is launched with it
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        from head_latent_attention_06_amd import build
+        build.build()
+    return mla.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for s in range(6):
+        assert mla.status_string(s).startswith("MLA_")
+    assert "unknown" in mla.status_string(99)
+
+
+def _cfg(**kw):
+    c = mla.Config(**kw)
+    return c._c()
+
+
+def test_workspace_sizes(lib):
+    n = ctypes.c_size_t()
+    assert lib.mla_decode_workspace_size(ctypes.byref(_cfg()), 64, 1, 4097, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value > 64 * 128 * 512 * 2
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_cfg()), 1, 8192, 0, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value > 8192 * 128 * 576 * 2
+    assert lib.mla_decode_num_splits(ctypes.byref(_cfg()), 64, 1, 4097) >= 64
+    assert lib.mla_decode_num_splits(ctypes.byref(_cfg()), 0, 1, 4097) == 0
+
+
+def test_unsupported_shapes_rejected(lib):
+    n = ctypes.c_size_t()
+    bad = [_cfg(d_c=256), _cfg(d_rope=32), _cfg(n_heads=48), _cfg(page_size=48),
+           _cfg(d_c=2048, dtype=__import__("torch").float32)]
+    for c in bad:
+        assert lib.mla_decode_workspace_size(ctypes.byref(c), 1, 1, 10, ctypes.byref(n)) == mla.MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_workspace_size(ctypes.byref(_cfg(n_heads=0)), 1, 1, 10, ctypes.byref(n)) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_workspace_size(None, 1, 1, 10, ctypes.byref(n)) == mla.MLA_ERR_INVALID_ARG
+
+
+def _cache(pool=FAKE, pages=10, bt=FAKE, maxp=4):
+    return mla._Cache(pool, pages, bt, maxp, None)
+
+
+def test_decode_argument_errors_before_launch(lib):
+    c = ctypes.byref(_cfg())
+    P = FAKE
+    k = ctypes.byref(_cache())
+    call = lambda **o: lib.mla_decode(c, o.get("k", k), o.get("lens", P), o.get("maxkv", 100), o.get("B", 2),
+                                      o.get("sq", 1), o.get("qn", P), o.get("qp", P), P, P, o.get("out", P),
+                                      o.get("ws", P), o.get("wsb", 0), None)
+    assert call(lens=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(qn=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(qn=FAKE + 2) == mla.MLA_ERR_INVALID_ARG               # misaligned
+    assert call(B=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call(B=0) == mla.MLA_OK                                    # empty batch: nothing to do
+    assert call(maxkv=0) == mla.MLA_ERR_INVALID_ARG                   # below s_q
+    assert call(maxkv=4 * 64 + 1) == mla.MLA_ERR_OUT_OF_RANGE         # past the block table
+    assert call(k=ctypes.byref(_cache(pool=None))) == mla.MLA_ERR_INVALID_ARG
+    assert call(k=ctypes.byref(_cache(pages=0))) == mla.MLA_ERR_INVALID_ARG
+    assert call(wsb=16) == mla.MLA_ERR_WORKSPACE                      # too small
+
+
+def test_prefill_and_append_argument_errors(lib):
+    c = ctypes.byref(_cfg())
+    k = ctypes.byref(_cache())
+    w = mla._Weights(*([FAKE] * 9))
+    assert lib.mla_prefill(c, k, ctypes.byref(w), FAKE, 1, 10, 0, FAKE, FAKE, 16, None) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_prefill(c, k, ctypes.byref(w), FAKE, 1, 10, 250, FAKE, FAKE, 1 << 40, None) == \
+        mla.MLA_ERR_OUT_OF_RANGE
+    w2 = mla._Weights(*([FAKE] * 8 + [None]))
+    assert lib.mla_prefill(c, k, ctypes.byref(w2), FAKE, 1, 10, 0, FAKE, FAKE, 1 << 40, None) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill(c, k, ctypes.byref(w), FAKE, 0, 10, 0, FAKE, FAKE, 0, None) == mla.MLA_OK
+    assert lib.mla_cache_append(c, k, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, None) == mla.MLA_OK
+    assert lib.mla_cache_append(c, k, None, FAKE, FAKE, FAKE, FAKE, 5, 1, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(c, k, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_project_kv(c, k, ctypes.byref(w), FAKE, 1, 10, 0, FAKE, 16, None) == mla.MLA_ERR_WORKSPACE

@@ -86,3 +86,57 @@ def test_decode_v3_batch64_context4096():
     print(f"rel_l2(sampled)={err:.3e}")
     assert err <= BF16_TOL
     assert int(cache.err_flags.item()) == 0
+
+
+def test_decode_long_context_131072():
+    """B=4 sequences x 131072 cached tokens (+1 new): long split chains and merge."""
+    ctx = mi.config_context_lens(4)
+    inp = _case(4, ctx, 1)
+    cfg, cache, bt, t = decode_setup(inp, config_id=4)
+    got = host(run_decode(cfg, cache, t, int(inp.kv_lens.max())))
+    assert np.isfinite(got).all()
+    seqs, heads = [0, 3], [5, 100]
+    ref = oracle_decode(inp, seqs=seqs, heads=heads)
+    err = rel_l2(got[seqs][:, :, heads], ref)
+    print(f"rel_l2(sampled)={err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_decode_ragged_paged_s_q2():
+    """B=128, context ~ U{1..32768}, 2 causal queries per sequence, shuffled pages."""
+    ctx = mi.config_context_lens(5)
+    inp = _case(5, ctx, 2)
+    cfg, cache, bt, t = decode_setup(inp, config_id=5)
+    got = host(run_decode(cfg, cache, t, int(inp.kv_lens.max())))
+    assert np.isfinite(got).all()
+    order = np.argsort(inp.kv_lens)
+    seqs = [int(order[0]), int(order[1]), int(order[64]), int(order[-1])]  # shortest, middle, longest
+    heads = [0, 77]
+    ref = oracle_decode(inp, seqs=seqs, heads=heads)
+    err = rel_l2(got[seqs][:, :, heads], ref)
+    print(f"kv_lens={inp.kv_lens[seqs]} rel_l2(sampled)={err:.3e}")
+    assert err <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
+
+
+def test_decode_bad_page_and_length_are_flagged():
+    """Block-table entries outside the pool and lengths past the bound are
+    reported in err_flags; the kernels skip them (no access outside the pool)."""
+    import head_latent_attention_06_amd as mla
+    inp = _case(106, [100, 100], 1)
+    cfg, cache, bt, t = decode_setup(inp, config_id=106)
+    bad = cache.block_table.clone()
+    bad[0, 1] = cache.pool.shape[0] + 5           # page id past the pool
+    cache_bad = mla.PagedCache(cache.pool, bad, cache.err_flags)
+    run_decode(cfg, cache_bad, t, 101)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) & mla.MLA_FLAG_BAD_PAGE
+    cache.err_flags.zero_()
+    t2 = dict(t)
+    t2["kv_lens"] = torch.tensor([101, 500], dtype=torch.int32, device="cuda")  # 500 > max_kv_len
+    out = run_decode(cfg, cache, t2, 101)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) & mla.MLA_FLAG_BAD_LEN
+    assert torch.all(out[1].float() == 0)          # the invalid row is written as zeros
+    ref = oracle_decode(inp, seqs=[0])
+    assert rel_l2(host(out)[0:1], ref) <= BF16_TOL  # the valid row is unaffected

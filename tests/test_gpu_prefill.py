@@ -89,3 +89,36 @@ def test_prefill_v3_small_bf16_full():
         gathered = om.paged_gather(host(cache.pool), cache.block_table.cpu().numpy(), b, 96, s.page_size)
         assert rel_l2(gathered, rows) <= BF16_TOL
     assert int(cache.err_flags.item()) == 0
+
+
+def test_prefill_v3_8192_sampled():
+    """B=1, L=8192 causal prefill at DeepSeek-V3 shapes; oracle on sampled (token, head)."""
+    s = mi.V3
+    L = 8192
+    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 3, 1, L)
+    got = host(out)[0]
+    assert np.isfinite(got).all()
+    tokens = np.array([0, 1, 31, 32, 1000, 4095, 4096, 8190, 8191])
+    heads = [0, 63, 127]
+    ref, rows = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=tokens, heads=heads)
+    err = rel_l2(got[tokens][:, heads], ref)
+    print(f"rel_l2(sampled)={err:.3e}")
+    assert err <= BF16_TOL
+    gathered = om.paged_gather(host(cache.pool), cache.block_table.cpu().numpy(), 0, L, s.page_size)
+    assert rel_l2(gathered, rows) <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
+
+
+def test_prefill_bf16_chunked_matches_whole():
+    """V3 shapes: prefill of 160 tokens == 96 tokens, then 64 more at start_pos=96."""
+    s = mi.V3
+    w = mi.weights(32, s)
+    h = mi.hidden(32, s, 1, 160)
+    cfg, cache, _, _, out_all = _prefill(s, torch.bfloat16, 32, 1, 160, w=w, h=h)
+    bt, npages = mi.block_table(33, [160], s.page_size, shuffle=True)
+    cache2 = paged_cache(cfg, npages, bt)
+    _prefill(s, torch.bfloat16, 32, 1, 96, w=w, h=h[:, :96], cache=cache2)
+    _, _, _, _, out_tail = _prefill(s, torch.bfloat16, 32, 1, 64, start_pos=96, w=w, h=h[:, 96:], cache=cache2)
+    ref, _ = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=np.arange(96, 160))
+    assert rel_l2(host(out_tail)[0], ref) <= BF16_TOL
+    assert rel_l2(host(out_tail)[0], host(out_all)[0, 96:]) <= 5e-3
