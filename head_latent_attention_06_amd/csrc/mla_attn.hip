@@ -10,28 +10,30 @@
 // W_i^UV is applied to o_lat afterwards by a GEMM.
 //
 // bf16 kernel design (gfx950, one workgroup = 4 waves = 128 heads of one token
-// over one key split):
+// over one chunk of keys):
 //  * Every head of a token reads the same 576-value cache rows, so a 32-key
-//    tile is staged once through LDS and consumed by all 128 heads: the cache
-//    is read from HBM exactly once per (token, split).
+//    tile is staged once in LDS and consumed by all 128 heads: the cache is
+//    read from HBM exactly once per (token, chunk).
+//  * Tiles move HBM -> LDS with direct-to-LDS buffer loads (no registers), three
+//    tiles in flight over a ring of four LDS stages; keys past the visible
+//    range fall outside the buffer resource and arrive as zeros.  The 16-byte
+//    chunks of key row r sit at chunk index c ^ f(r), f(r) = (2r ^ r/4) & 7,
+//    which keeps every LDS read pattern below free of bank conflicts.
 //  * Wave w owns 32 heads.  Scores are computed transposed, S^T = K Q^T, on
 //    v_mfma_f32_32x32x16_bf16 (keys on M, heads on N, 576 dims on K), with the
-//    wave's Q^T fragments held in registers for the whole split.  In that
+//    wave's Q^T fragments held in registers for the whole chunk.  In that
 //    layout each lane holds 16 scores of ONE head, so the exponentiated scores
-//    are already the B operand of O^T = V^T P^T (32x32x16 MFMA, dims on M,
-//    heads on N, keys on K) and the per-head softmax rescale of O^T is a
-//    per-lane scalar.
-//  * V^T is built while staging: each thread loads 8 keys x 8 dims, transposes
-//    them in registers and writes 16-byte rows of a [dim][key] LDS tile whose
-//    key order matches the MFMA k-slot order of P^T.  Row permutation
-//    dim ^ ((dim >> 3) & 15) with an 80-byte stride keeps both the transposed
-//    writes and the MFMA operand reads free of bank conflicts.
+//    are already the B operand of O^T = V^T P^T (dims on M, heads on N, keys
+//    on K) and the per-head softmax rescale of O^T is a per-lane scalar.
+//  * V^T operands come straight from the row-major key tile through
+//    ds_read_b64_tr_b16 (gfx950 transposing LDS read): within each 16-lane
+//    group, output lane 4a+e receives element e of source lanes a, a+4, a+8,
+//    a+12, so four source lanes pointing at four key rows give each output
+//    lane four keys of one latent dim.
 //  * Online softmax in the log2 domain; the running max is only raised when
 //    a tile's max exceeds it by more than 8 (p <= 256 stays exact in fp32),
-//    so the 256-register accumulator is rescaled rarely.  Row max / sum across
-//    the two lane halves use v_permlane32_swap.
-//  * Double-buffered LDS (2 x 78 KB): tile t+1 is written to LDS and tile t+2
-//    fetched into registers while tile t is being consumed.
+//    so the 256-register O^T accumulator (kept in AGPRs) is rescaled rarely.
+//    Row max / sum across the two lane halves use v_permlane32_swap.
 #include <math.h>
 
 #include "mla_device.h"
@@ -42,11 +44,10 @@ namespace {
 
 constexpr int DC = 512, DR = 64, ROW = DC + DR;  // cached row: c^KV then k^R
 constexpr int TILE = 32;                         // keys per LDS tile
-constexpr int KSTR = ROW * 2 + 16;               // bytes per key row of the K tile
-constexpr int VSTR = 80;                         // bytes per dim row of the V^T tile
-constexpr int KBYTES = TILE * KSTR;
-constexpr int VBYTES = DC * VSTR;
-constexpr int STAGE = KBYTES + VBYTES;
+constexpr int RB = ROW * 2;                      // bytes per key row (1152, unpadded)
+constexpr int STAGE = TILE * RB;                 // 36864 bytes per tile
+constexpr int NSTAGE = 4, DEPTH = 3;             // LDS ring, tiles in flight
+constexpr int DMA_PER_THREAD = STAGE / 16 / 256; // 9 16-byte loads per thread per tile
 constexpr int WG_HEADS = 128;
 constexpr int MAX_SPLIT_PAGES = 1536;            // page ids of one split, staged in LDS
 constexpr int FLAG_BAD_PAGE = 1, FLAG_BAD_LEN = 4;
@@ -65,6 +66,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// A pointer the compiler cannot prove wave-uniform, made uniform (SGPRs).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// LDS chunk swizzle of key row r (chunk c of the row sits at c ^ kswz(r))
+__device__ __forceinline__ int kswz(int r) { return ((r << 1) ^ (r >> 2)) & 7; }
+// 16 bytes per lane from buffer offset voff into LDS at lds_addr + 16 * lane.
+// Issued in asm so the compiler's wait-count pass does not put a full vmcnt
+// wait in front of every later LDS access; the kernel waits explicitly.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+__device__ __forceinline__ u32x2 lds_tr16(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) unsigned char*)p);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Multiply the 16 AGPRs of one accumulator tuple by alpha, one register at a
@@ -85,7 +115,7 @@ __device__ __forceinline__ void scale_acc_tuple(f32x16& t, float alpha) {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
   __shared__ int split_pages[MAX_SPLIT_PAGES];
 
   const int n_hg = (a.H + WG_HEADS - 1) / WG_HEADS;
@@ -147,71 +177,19 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) acc[x][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Staging.  Wave w stages key slot group w: keys 16*(w/2) + 4*(w%2) +
-  // 8*(e/4) + (e%4), e = 0..7 (wave-uniform offsets), latent dims
-  // 8*lane .. 8*lane+7; thread tid also stages rope dims 8*(tid%8) .. of key tid/8.
-  const int lat_row = 16 * (wave >> 1) + 4 * (wave & 1);
-  const int rope_off = (tid >> 3) * ROW * 2 + DC * 2 + 16 * (tid & 7);
-  unsigned char* const kw0 = smem + (16 * (wave >> 1) + 4 * (wave & 1)) * KSTR + 16 * lane;
-  unsigned char* const rw0 = smem + (tid >> 3) * KSTR + DC * 2 + 16 * (tid & 7);
-  // V^T layout: dim d lives in physical row vrow(d) = d ^ ((d >> 3) & 15) (80-byte
-  // rows), key slot group q at q * 16 bytes.  Both the staging writes (lanes
-  // cover dims 8*lane + j) and the MFMA reads (32 consecutive dims) are then
-  // free of bank conflicts with 16-lane phases over 64 banks and with 8-lane
-  // phases over 32 banks.  For dims 8*lane + j the row is
-  // wrow + (j ^ (lane & 7)) with wrow = 16*(lane/2) + 8*((lane ^ (lane >> 3)) & 1).
-  const int wrow = 16 * (lane >> 1) + 8 * ((lane ^ (lane >> 3)) & 1);
-  const int wl3 = lane & 7;
-  unsigned char* const vw0 = smem + KBYTES + wave * 16;
-  const unsigned char* const kr0 = smem + l32 * KSTR + hi * 16;
-  // reads: dim 32*blk + l32 -> row 32*blk + (l32 ^ ((4*(blk & 3) + (l32 >> 3)) & 15))
-  const unsigned char* vr[4];
+  // ---- tile loads: wave w's instruction i covers LDS chunks (4i + w)*64 + lane
+  // of the stage; LDS chunk P holds key row P / 72, row chunk (P % 72) ^ kswz(row).
+  int32_t dma_off[DMA_PER_THREAD];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-    vr[b] = smem + KBYTES + (l32 ^ ((4 * b + (l32 >> 3)) & 15)) * VSTR + hi * 16;
+  for (int i = 0; i < DMA_PER_THREAD; ++i) {
+    const int P = (4 * i + wave) * 64 + lane;
+    const int r = P / 72, c = (P % 72) ^ kswz(P / 72);
+    dma_off[i] = r * RB + c * 16;
+  }
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  u32x4 sv[8], sr;
-
-#define MLA_LOAD_TILE(T)                                                                          \
-  {                                                                                               \
-    const int kb_ = k0 + (T) * TILE;                                                              \
-    const int page_ = __builtin_amdgcn_readfirstlane(split_pages[kb_ / a.page_size - pg_first]);  \
-    const bool pok_ = page_ >= 0 && (int64_t)page_ < a.num_pages;                                 \
-    if (!pok_ && tid == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);                   \
-    const bf16* base_ =                                                                           \
-        (const bf16*)a.pool + ((int64_t)(pok_ ? page_ : 0) * a.page_size + (kb_ % a.page_size)) * ROW; \
-    const int nvalid_ = pok_ ? min(TILE, k1 - kb_) : 0;                                           \
-    /* one descriptor per staged key: its base is that key's row (a wave-uniform */               \
-    /* offset), its size 0 when the key is past the visible range -> loads zero */                \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                               \
-      const int key_ = lat_row + 8 * (e >> 2) + (e & 3);                                          \
-      const __amdgpu_buffer_rsrc_t r_ = make_rsrc(base_ + key_ * ROW, key_ < nvalid_ ? ROW * 2 : 0); \
-      sv[e] = buf_ld16(r_, 16 * lane);                                                            \
-    }                                                                                             \
-    sr = buf_ld16(make_rsrc(base_, nvalid_ * ROW * 2), rope_off);                                 \
-  }
-
-#define MLA_STORE_TILE(BUF)                                                                       \
-  {                                                                                               \
-    const int off_ = (BUF) * STAGE;                                                               \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                 \
-      st16(kw0 + off_ + (8 * (e >> 2) + (e & 3)) * KSTR, sv[e]);                                  \
-    st16(rw0 + off_, sr);                                                                         \
-    /* transpose 8 keys x 8 dims: V^T row 8*lane + d gets the keys in slot order */               \
-    _Pragma("unroll") for (int c2 = 0; c2 < 4; ++c2) {                                            \
-      u32x4 o0_, o1_;                                                                             \
-      _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) {                                          \
-        const uint32_t x0_ = sv[2 * r2][c2], x1_ = sv[2 * r2 + 1][c2];                            \
-        o0_[r2] = (x0_ & 0xFFFFu) | (x1_ << 16);                                                  \
-        o1_[r2] = (x0_ >> 16) | (x1_ & 0xFFFF0000u);                                              \
-      }                                                                                           \
-      st16(vw0 + off_ + (wrow + ((2 * c2) ^ wl3)) * VSTR, o0_);                                   \
-      st16(vw0 + off_ + (wrow + ((2 * c2 + 1) ^ wl3)) * VSTR, o1_);                               \
-    }                                                                                             \
-  }
-
-  // The split's page ids (the block-table read is kept off the tile pipeline).
+  // The chunk's page ids (the block-table read is kept off the tile pipeline).
   const int pg_first = k0 / a.page_size;
   const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
   for (int i = tid; i < n_pages; i += 256) {
@@ -220,14 +198,60 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
+  auto issue_tile = [&](int t) {
+    const int kb = k0 + t * TILE;
+    const int page = __builtin_amdgcn_readfirstlane(split_pages[kb / a.page_size - pg_first]);
+    const bool pok = page >= 0 && (int64_t)page < a.num_pages;
+    if (!pok && tid == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
+    // rows of the tile are contiguous within one page; rows past k1 (and a
+    // bad page) lie outside the resource and load as zeros
+    const bf16* base = (const bf16*)a.pool + ((int64_t)(pok ? page : 0) * a.page_size + (kb % a.page_size)) * ROW;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(uniform_ptr(base), __builtin_amdgcn_readfirstlane(pok ? min(TILE, k1 - kb) * RB : 0));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_addr + (t % NSTAGE) * STAGE + wave * 1024);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(r, dst + i * 4096, dma_off[i]);
+  };
+
+  // QK operand (row l32, 16-byte chunk 2j + hi): per-lane offsets for j % 4,
+  // plus 128 bytes per 4 k steps
+  int qk_off[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) qk_off[jj] = l32 * RB + (((2 * jj + hi) ^ kswz(l32)) * 16);
+  // V^T operand via transposing reads: for k step q, read r (keys 16q+8r+4hi+j/4)
+  // and dim block blk: row = 16q + 8r + rl, chunk = 4blk + 2g1 + (j&3)/2, half j&1
+  const int g1 = (lane >> 4) & 1, jl = lane & 15;
+  const int rl = 4 * hi + (jl >> 2);
+  int pv_off[2][2][2];  // [q][r][blk & 1]; + (blk >> 1) * 128 bytes
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int bo = 0; bo < 2; ++bo) {
+        const int row = 16 * q + 8 * r + rl;
+        const int c = 4 * bo + 2 * g1 + ((jl & 3) >> 1);
+        pv_off[q][r][bo] = row * RB + ((c ^ kswz(row)) * 16) + 8 * (jl & 1);
+      }
+
   const int ntiles = (k1 - k0 + TILE - 1) / TILE;
-  MLA_LOAD_TILE(0);
-  MLA_STORE_TILE(0);
-  if (ntiles > 1) MLA_LOAD_TILE(1);
+#pragma unroll
+  for (int p = 0; p < DEPTH; ++p)
+    if (p < ntiles) issue_tile(p);
+
   for (int t = 0; t < ntiles; ++t) {
+    // this thread's loads of tile t are done once at most the later tiles'
+    // loads are outstanding; the barrier then makes every thread's visible
+    const int later = min(DEPTH - 1, ntiles - 1 - t);
+    if (later >= 2) wait_vmcnt<2 * DMA_PER_THREAD>();
+    else if (later == 1) wait_vmcnt<DMA_PER_THREAD>();
+    else wait_vmcnt<0>();
     __syncthreads();
+    // the stage of tile t + DEPTH last held tile t - 1, which every wave has
+    // finished reading before the barrier
+    if (t + DEPTH < ntiles) issue_tile(t + DEPTH);
     {  // waves past the last head compute on zero queries and store nothing
-      const int off = (t & 1) * STAGE;
+      const unsigned char* K = smem + (t % NSTAGE) * STAGE;
       const int kb = k0 + t * TILE;
       // ---- S^T[key][head] for the 32 keys of the tile, accumulated in VGPRs.
       // K fragments are read KW MFMAs ahead of use (one wave per SIMD: nothing
@@ -235,11 +259,14 @@ void attn_bf16_kernel(AttnArgs a) {
       constexpr int KW = 3;
       u32x4 kf[KW];
 #pragma unroll
-      for (int j = 0; j < KW - 1; ++j) kf[j] = *(const u32x4*)(kr0 + off + j * 32);
+      for (int j = 0; j < KW - 1; ++j) kf[j] = *(const u32x4*)(K + qk_off[j & 3] + 128 * (j >> 2));
       f32x16 s;
 #pragma unroll
       for (int j = 0; j < 36; ++j) {
-        if (j + KW - 1 < 36) kf[(j + KW - 1) % KW] = *(const u32x4*)(kr0 + off + (j + KW - 1) * 32);
+        if (j + KW - 1 < 36) {
+          const int jn = j + KW - 1;
+          kf[jn % KW] = *(const u32x4*)(K + qk_off[jn & 3] + 128 * (jn >> 2));
+        }
         if (j == 0) {
           asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(kf[0]), "v"(qf[0]));
         } else if (j < 35) {
@@ -254,9 +281,16 @@ void attn_bf16_kernel(AttnArgs a) {
       // The first V^T fragments do not depend on the softmax: start them now.
       constexpr int VW = 3;  // V fragments in flight
       u32x4 vf[VW];
+      auto load_v = [&](int m) {  // MFMA m: k step m >> 4, dim block m & 15
+        const int q = m >> 4, blk = m & 15;
+        const u32x2 lo = lds_tr16(K + pv_off[q][0][blk & 1] + 128 * (blk >> 1));
+        const u32x2 hv = lds_tr16(K + pv_off[q][1][blk & 1] + 128 * (blk >> 1));
+        return u32x4{lo[0], lo[1], hv[0], hv[1]};
+      };
 #pragma unroll
-      for (int i = 0; i < VW - 1; ++i) vf[i] = *(const u32x4*)(vr[i & 3] + off + i * 32 * VSTR);
+      for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
       __builtin_amdgcn_sched_barrier(0);
+
       // ---- online softmax (log2 domain); lane holds keys kb + 8*(i/4) + 4*hi + i%4 of head l32
       float mloc = -INFINITY;
       if (kb + TILE <= k1) {
@@ -301,11 +335,8 @@ void attn_bf16_kernel(AttnArgs a) {
       // k step, accumulated in AGPRs.  The wait states ahead of the first MFMA
       // cover VALU writes of the P fragments and of a rescaled accumulator.
 #pragma unroll
-      for (int m = 0; m < 32; ++m) {  // k step q = m/16, dim block m%16
-        if (m + VW - 1 < 32) {
-          const int mn = m + VW - 1;
-          vf[mn % VW] = *(const u32x4*)(vr[mn & 3] + off + (mn & 15) * 32 * VSTR + (mn >> 4) * 32);
-        }
+      for (int m = 0; m < 32; ++m) {
+        if (m + VW - 1 < 32) vf[(m + VW - 1) % VW] = load_v(m + VW - 1);
         if (m == 0) {
           asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0]) : "v"(vf[0]), "v"(pf[0]));
         } else {
@@ -315,13 +346,7 @@ void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (t + 1 < ntiles) {
-      MLA_STORE_TILE((t + 1) & 1);
-      if (t + 2 < ntiles) MLA_LOAD_TILE(t + 2);
-    }
   }
-#undef MLA_LOAD_TILE
-#undef MLA_STORE_TILE
   if (!wave_on) return;
   // wait states before VALU reads of accumulators last written by an MFMA
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
