@@ -160,22 +160,65 @@ def run_prefill_bench(steps: int, warmup: int, L: int = 8192):
     return dict(wall=wall, attn_ms=attn_ms, flops=prefill_flops(s, L), L=L)
 
 
-def cpu_baseline(inp, heads: int):
-    """The float64 oracle on sequence 0, `heads` of the 128 heads, all 4097 keys."""
+def cpu_baseline(inp, min_seconds: float):
+    """The float64 oracle on whole sequences of the decode workload (all 128
+    heads, every cached row), one after another until min_seconds have passed."""
     from oracle import mla_oracle as om
     s = inp.shape
-    rows = [inp.seq_rows(0)]
     t0 = time.perf_counter()
-    om.decode(rows, inp.kv_lens[:1], 1, inp.q_nope[:1], inp.q_pe[:1], inp.w_uk, inp.w_uv, s.d_c, s.scale,
-              heads=list(range(heads)))
+    n = 0
+    while n < len(inp.kv_lens) and (n == 0 or time.perf_counter() - t0 < min_seconds):
+        om.decode([inp.seq_rows(n)], inp.kv_lens[n:n + 1], 1, inp.q_nope[n:n + 1], inp.q_pe[n:n + 1], inp.w_uk,
+                  inp.w_uv, s.d_c, s.scale)
+        n += 1
     dt = time.perf_counter() - t0
-    # the sample is heads/128 of one sequence's step: that share of its latent rows
-    eq_bytes = int(inp.kv_lens[0]) * s.row * 2 * heads / s.n_heads
-    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    return dict(value=eq_bytes / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"float64 explicit MLA (numpy, {threads} BLAS threads), sequence 0 of the decode workload, "
-                       f"heads 0..{heads - 1} of 128 over all {int(inp.kv_lens[0])} cached rows, {dt:.1f} s; "
-                       f"scaled by the share of the latent rows it covers")
+    rows = int(inp.kv_lens[:n].sum())
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    return dict(value=rows * s.row * 2 / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"float64 explicit-form MLA (numpy, {threads} BLAS threads) on sequences 0..{n - 1} of the "
+                       f"decode workload ({rows} cached rows, all 128 heads), {dt:.1f} s; value = their latent-row "
+                       f"bytes / time")
+
+
+def copy_calibration(n_bytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n_bytes, "bytes_written": n_bytes, "launches": reps}}))
+
+
+def run_prefill_summary(args) -> dict:
+    steps = max(2, args.steps // 4)
+    p = run_prefill_bench(steps, max(1, args.warmup // 2))
+    pms = p["wall"] / steps * 1e3
+    f = p["flops"]
+    achieved = f["attention"] / (p["attn_ms"] * 1e-3) / 1e12
+    return {
+        "workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention",
+        "ms_per_step": round(pms, 3), "tflops_executed": round(f["total"] / (pms * 1e-3) / 1e12, 1),
+        "tokens_per_s": round(p["L"] / (pms * 1e-3), 1),
+        "explicit_equivalent_tflops": round(f["explicit_equivalent_total"] / (pms * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "kernel_ms": round(p["attn_ms"], 4),
+                     "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def measured_traffic(path: str = os.path.join(ROOT, "profiles", "attn_bf16_decode_b64_ctx4096_traffic.md")):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or the kernel source changed after it was taken."""
+    import hashlib
+    try:
+        kv = dict(l.split(":", 1) for l in open(path).read().splitlines() if l.startswith(("traffic_", "source_")))
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "head_latent_attention_06_amd", "csrc", "mla_attn.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256", "").strip():
+        return None
+    return int(kv["traffic_bytes_per_launch"].strip())
 
 
 def main():
@@ -184,8 +227,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill workload (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -193,7 +239,13 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill_summary(args)}), flush=True)
+        return
     d = run_decode_bench(args.steps, args.warmup)
     ms = d["wall"] / args.steps * 1e3
     value = d["latent_bytes"] / (ms * 1e-3) / 1e9
@@ -206,27 +258,15 @@ def main():
                                "n_h=128, d_h=128, d_c=512, d_h^R=64, 64-token pages, shuffled block table",
                    "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(d["attn_ms"], 5),
                      "algorithmic_bytes": d["latent_bytes"],
                      "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
     }
     if not args.no_prefill:
-        p = run_prefill_bench(max(2, args.steps // 4), max(1, args.warmup // 2))
-        pms = p["wall"] / max(2, args.steps // 4) * 1e3
-        f = p["flops"]
-        res["prefill"] = {
-            "workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention",
-            "ms_per_step": round(pms, 3), "tflops_executed": round(f["total"] / (pms * 1e-3) / 1e12, 1),
-            "tokens_per_s": round(p["L"] / (pms * 1e-3), 1),
-            "explicit_equivalent_tflops": round(f["explicit_equivalent_total"] / (pms * 1e-3) / 1e12, 1),
-            "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "kernel_ms": round(p["attn_ms"], 4),
-                         "achieved": round(f["attention"] / (p["attn_ms"] * 1e-3) / 1e12, 1),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(f["attention"] / (p["attn_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        }
+        res["prefill"] = run_prefill_summary(args)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(d["inp"], args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(d["inp"], args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
