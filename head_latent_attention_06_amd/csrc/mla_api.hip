@@ -92,7 +92,7 @@ DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, i
   d.o_lat = cv.take(rows * H * c->d_c * e);
   if (bf16) {
     d.max_items = max_plan_items(c, rows, max_kv, DECODE_TARGET_ITEMS);
-    d.plan = (int32_t*)cv.take((rows + 3) * 4);
+    d.plan = (int32_t*)cv.take(plan_ints(rows, d.max_items) * 4);
     d.part_o = cv.take(d.max_items * H * c->d_c * 2);
     d.part_ml = (float*)cv.take(d.max_items * H * 2 * 4);
   }
@@ -127,7 +127,7 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, i
     const int32_t kv_end = start_pos + L;
     p.split = kv_end > max_chunk_keys(c);
     p.max_items = max_plan_items(c, T, kv_end, 0);
-    p.plan = (int32_t*)cv.take((T + 3) * 4);
+    p.plan = (int32_t*)cv.take(plan_ints(T, p.max_items) * 4);
     if (p.split) {
       p.part_o = cv.take(p.max_items * H * c->d_c * 2);
       p.part_ml = (float*)cv.take(p.max_items * H * 2 * 4);

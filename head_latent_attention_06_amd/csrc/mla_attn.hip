@@ -117,36 +117,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
   __shared__ int split_pages[MAX_SPLIT_PAGES];
+  __shared__ u32x4 p_xchg[4 * 2 * 64];   // P^T fragments [head block][k step][lane]
+  __shared__ float alpha_xchg[4][32];    // per head: rescale factor of the current tile
+  __shared__ float lsum_xchg[4][32];     // per head: softmax sum of the chunk
+  __shared__ __attribute__((aligned(4))) unsigned char flag_xchg[4];  // head block raised its max this tile
 
   const int n_hg = (a.H + WG_HEADS - 1) / WG_HEADS;
   const int tid = threadIdx.x;
-  const int n_items = a.plan[0];
-  const int chunk = a.plan[1];
-  // The grid is an upper bound on the plan's items, so blocks map to items in
-  // launch order: the real items are then spread round-robin over all XCDs.
-  // With longest_first they run in reverse plan order (rows with most keys are
-  // planned last).
+  // The plan lists this workgroup's item in launch order (the grid is an
+  // upper bound on the items; entries past the last item are empty).
   const int bid = (int)blockIdx.x / n_hg, hg = (int)blockIdx.x % n_hg;
-  if (bid >= n_items) return;
-  const int w = a.longest_first ? n_items - 1 - bid : bid;
-  const int n_rows = a.B * a.s_q;
-  const int32_t* row_off = a.plan + 2;
-  int lo = 0, hi_r = n_rows - 1;  // last row r with row_off[r] <= w
-  while (lo < hi_r) {
-    const int mid = (lo + hi_r + 1) >> 1;
-    if (row_off[mid] <= w) lo = mid; else hi_r = mid - 1;
-  }
-  const int row = lo;
-  const int split = w - row_off[row];
-  const int n_split_row = row_off[row + 1] - row_off[row];
-  const int b = row / a.s_q, sq = row % a.s_q;
-  bool len_ok;
-  const int kv = kv_len_of(a, b, len_ok);
-  if (!len_ok) return;  // the plan gives such rows no items
-  const int qpos = kv - a.s_q + sq;
-  const int k0 = split * chunk;
-  const int k1 = min(k0 + chunk, qpos + 1);
+  const int4 item = reinterpret_cast<const int4*>(a.plan + plan_info_offset((int64_t)a.B * a.s_q))[bid];
+  const int row = __builtin_amdgcn_readfirstlane(item.x);
+  const int k0 = __builtin_amdgcn_readfirstlane(item.y), k1 = __builtin_amdgcn_readfirstlane(item.z);
+  const int w = __builtin_amdgcn_readfirstlane(item.w) >> 1;         // item index: slot of a partial
+  const bool multi = (__builtin_amdgcn_readfirstlane(item.w) & 1) != 0;  // row has several items
   if (k0 >= k1) return;
+  const int b = row / a.s_q;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -155,6 +142,68 @@ void attn_bf16_kernel(AttnArgs a) {
   const int64_t qrow = row;
   const float scale_log2 = a.scale * LOG2E;
 
+  // ---- the chunk's page ids, staged once (keeps block-table reads off the pipeline)
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int pg_first = k0 / a.page_size;
+  const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
+  for (int i = tid; i < n_pages; i += 256) {
+    const int pidx = pg_first + i;
+    split_pages[i] = pidx < a.max_pages ? bt[pidx] : -1;
+  }
+  __syncthreads();
+
+  // ---- tile loads: wave w's instruction i covers LDS chunks (4i + w)*64 + lane
+  // of the stage; LDS chunk P holds key row P / 72, row chunk (P % 72) ^ kswz(row).
+  int32_t dma_off[DMA_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_THREAD; ++i) {
+    const int P = (4 * i + wave) * 64 + lane;
+    const int r = P / 72, c = (P % 72) ^ kswz(P / 72);
+    dma_off[i] = r * RB + c * 16;
+  }
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+  // Issue cursor: the next tile to load sits at key offset cur_off of page
+  // slot cur_slot of the chunk (tiles never straddle a page).  Scalar state,
+  // advanced by one tile per issue, so no division on the issue path.
+  int cur_slot = 0, cur_off = k0 % a.page_size, cur_tile = 0;
+  const uint64_t pool_addr = (uint64_t)(uintptr_t)a.pool;
+  const uint32_t page_bytes = (uint32_t)a.page_size * RB;
+  const uint32_t num_pages = (uint32_t)min<int64_t>(a.num_pages, 0x7fffffff);
+  bool bad_page = false;  // reported once, after the loop
+  struct TileDma {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t dst;
+  };
+  auto prep_tile = [&](int page_id) {  // resource of the cursor's tile, then advance
+    // 32-bit scalar arithmetic only: a negative id fails the unsigned compare
+    const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_id);
+    const bool pok = page < num_pages;
+    // rows of the tile are contiguous within one page; rows past k1 (and a
+    // bad page) lie outside the resource and load as zeros
+    const int kb = k0 + cur_tile * TILE;
+    const uint64_t addr = pool_addr + (uint64_t)(pok ? page : 0u) * page_bytes + (uint32_t)cur_off * RB;
+    TileDma d;
+    d.r = make_rsrc((const void*)(uintptr_t)addr, pok ? min(TILE, k1 - kb) * RB : 0);
+    d.dst = smem_addr + (cur_tile % NSTAGE) * STAGE + wave * 1024;
+    cur_tile += 1;
+    cur_off += TILE;
+    if (cur_off == a.page_size) {
+      cur_off = 0;
+      cur_slot += 1;
+    }
+    bad_page |= !pok;
+    return d;
+  };
+  auto issue_next = [&](int page_id) {
+    const TileDma d = prep_tile(page_id);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(d.r, d.dst + i * 4096, dma_off[i]);
+  };
+  const int ntiles = (k1 - k0 + TILE - 1) / TILE;
+
+  // ---- prologue loads, in the order the first tile needs them: tile 0, the
+  // queries, then tiles 1 .. DEPTH-1 (vector loads complete in issue order).
+  issue_next(split_pages[0]);
   // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
   // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
   u32x4 qf[36];
@@ -169,49 +218,30 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
   }
+  // Wait for the queries (and tile 0) here: left to the compiler, the wait
+  // would sit inside the tile loop in front of the MFMAs that read them and
+  // would drain the tile loads in flight on every pass.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+               "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]));
+  asm volatile("" ::"v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]), "v"(qf[18]),
+               "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]));
+  asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
+               "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
+#pragma unroll
+  for (int p = 1; p < DEPTH; ++p)
+    if (p < ntiles) issue_next(split_pages[cur_slot]);
+  // page of the next tile to issue, fetched one tile early to keep the LDS
+  // latency off the issue path
+  int next_page = DEPTH < ntiles ? split_pages[cur_slot] : 0;
 
+  // Accumulator O^T for this wave's 128 latent dims (4 blocks of 32) and all
+  // 128 heads of the workgroup (4 blocks of 32): acc[4 * d + hb].
   f32x16 acc[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[x][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // ---- tile loads: wave w's instruction i covers LDS chunks (4i + w)*64 + lane
-  // of the stage; LDS chunk P holds key row P / 72, row chunk (P % 72) ^ kswz(row).
-  int32_t dma_off[DMA_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_THREAD; ++i) {
-    const int P = (4 * i + wave) * 64 + lane;
-    const int r = P / 72, c = (P % 72) ^ kswz(P / 72);
-    dma_off[i] = r * RB + c * 16;
-  }
-  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  // The chunk's page ids (the block-table read is kept off the tile pipeline).
-  const int pg_first = k0 / a.page_size;
-  const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
-  for (int i = tid; i < n_pages; i += 256) {
-    const int pidx = pg_first + i;
-    split_pages[i] = pidx < a.max_pages ? bt[pidx] : -1;
-  }
-  __syncthreads();
-
-  auto issue_tile = [&](int t) {
-    const int kb = k0 + t * TILE;
-    const int page = __builtin_amdgcn_readfirstlane(split_pages[kb / a.page_size - pg_first]);
-    const bool pok = page >= 0 && (int64_t)page < a.num_pages;
-    if (!pok && tid == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
-    // rows of the tile are contiguous within one page; rows past k1 (and a
-    // bad page) lie outside the resource and load as zeros
-    const bf16* base = (const bf16*)a.pool + ((int64_t)(pok ? page : 0) * a.page_size + (kb % a.page_size)) * ROW;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(uniform_ptr(base), __builtin_amdgcn_readfirstlane(pok ? min(TILE, k1 - kb) * RB : 0));
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_addr + (t % NSTAGE) * STAGE + wave * 1024);
-#pragma unroll
-    for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(r, dst + i * 4096, dma_off[i]);
-  };
+  float m_run = -INFINITY, l_run = 0.f;  // of head head0 + l32 (this wave's head block)
 
   // QK operand (row l32, 16-byte chunk 2j + hi): per-lane offsets for j % 4,
   // plus 128 bytes per 4 k steps
@@ -234,147 +264,224 @@ void attn_bf16_kernel(AttnArgs a) {
         pv_off[q][r][bo] = row * RB + ((c ^ kswz(row)) * 16) + 8 * (jl & 1);
       }
 
-  const int ntiles = (k1 - k0 + TILE - 1) / TILE;
+  // ---- per-tile pieces ----------------------------------------------------
+  // S^T[key][head] for the 32 keys of a tile and this wave's 32 heads, in
+  // VGPRs: 36 MFMAs over the 576 dims.  K fragments are read KW steps ahead.
+  constexpr int KW = 3;
+  u32x4 kf[KW];
+  auto qk_begin = [&](const unsigned char* K) {
 #pragma unroll
-  for (int p = 0; p < DEPTH; ++p)
-    if (p < ntiles) issue_tile(p);
-
-  for (int t = 0; t < ntiles; ++t) {
-    // this thread's loads of tile t are done once at most the later tiles'
-    // loads are outstanding; the barrier then makes every thread's visible
-    const int later = min(DEPTH - 1, ntiles - 1 - t);
-    if (later >= 2) wait_vmcnt<2 * DMA_PER_THREAD>();
-    else if (later == 1) wait_vmcnt<DMA_PER_THREAD>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    // the stage of tile t + DEPTH last held tile t - 1, which every wave has
-    // finished reading before the barrier
-    if (t + DEPTH < ntiles) issue_tile(t + DEPTH);
-    {  // waves past the last head compute on zero queries and store nothing
-      const unsigned char* K = smem + (t % NSTAGE) * STAGE;
-      const int kb = k0 + t * TILE;
-      // ---- S^T[key][head] for the 32 keys of the tile, accumulated in VGPRs.
-      // K fragments are read KW MFMAs ahead of use (one wave per SIMD: nothing
-      // else hides the LDS latency); sched_barrier pins that order.
-      constexpr int KW = 3;
-      u32x4 kf[KW];
+    for (int j = 0; j < KW - 1; ++j) kf[j] = *(const u32x4*)(K + qk_off[j & 3] + 128 * (j >> 2));
+  };
+  auto qk_step = [&](const unsigned char* K, int j, f32x16& sacc) {
+    if (j + KW - 1 < 36) {
+      const int jn = j + KW - 1;
+      kf[jn % KW] = *(const u32x4*)(K + qk_off[jn & 3] + 128 * (jn >> 2));
+    }
+    if (j == 0) {
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sacc) : "v"(kf[0]), "v"(qf[0]));
+    } else if (j < 35) {
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(kf[j % KW]), "v"(qf[j]));
+    } else {
+      // the trailing wait states let VALU read the MFMA result
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+          : "+v"(sacc) : "v"(kf[j % KW]), "v"(qf[j]));
+    }
+  };
+  // Online softmax (log2 domain) of one tile for this wave's heads, in three
+  // stages so it can run between the next tile's QK MFMAs.  Lane holds keys
+  // kb + 8*(i/4) + 4*hi + i%4 of head l32.  The scale is positive, so the max
+  // is taken on raw scores and the scale folded into the exponent's FMA.
+  float mloc;
+  auto sm_max = [&](f32x16& sc, int kb) {
+    mloc = -INFINITY;
+    if (kb + TILE <= k1) {
 #pragma unroll
-      for (int j = 0; j < KW - 1; ++j) kf[j] = *(const u32x4*)(K + qk_off[j & 3] + 128 * (j >> 2));
-      f32x16 s;
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
+    } else {
+      const int rem = k1 - kb - 4 * hi;
 #pragma unroll
-      for (int j = 0; j < 36; ++j) {
-        if (j + KW - 1 < 36) {
-          const int jn = j + KW - 1;
-          kf[jn % KW] = *(const u32x4*)(K + qk_off[jn & 3] + 128 * (jn >> 2));
-        }
-        if (j == 0) {
-          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(kf[0]), "v"(qf[0]));
-        } else if (j < 35) {
-          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[j % KW]), "v"(qf[j]));
-        } else {
-          // the trailing wait states let VALU read the MFMA result
-          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-              : "+v"(s) : "v"(kf[j % KW]), "v"(qf[j]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // The first V^T fragments do not depend on the softmax: start them now.
-      constexpr int VW = 3;  // V fragments in flight
-      u32x4 vf[VW];
-      auto load_v = [&](int m) {  // MFMA m: k step m >> 4, dim block m & 15
-        const int q = m >> 4, blk = m & 15;
-        const u32x2 lo = lds_tr16(K + pv_off[q][0][blk & 1] + 128 * (blk >> 1));
-        const u32x2 hv = lds_tr16(K + pv_off[q][1][blk & 1] + 128 * (blk >> 1));
-        return u32x4{lo[0], lo[1], hv[0], hv[1]};
-      };
-#pragma unroll
-      for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // ---- online softmax (log2 domain); lane holds keys kb + 8*(i/4) + 4*hi + i%4 of head l32
-      float mloc = -INFINITY;
-      if (kb + TILE <= k1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[i] *= scale_log2;
-          mloc = fmaxf(mloc, s[i]);
-        }
-      } else {
-        const int rem = k1 - kb - 4 * hi;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[i] = (8 * (i >> 2) + (i & 3) < rem) ? s[i] * scale_log2 : -INFINITY;
-          mloc = fmaxf(mloc, s[i]);
-        }
-      }
-      const float mt = pair_max32(mloc);
-      if (m_run == -INFINITY) {
-        m_run = mt;  // first tile: accumulator and sum are still zero
-      } else if (__any(mt > m_run + RESCALE_SLACK)) {
-        const float mn = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - mn);
-        l_run *= alpha;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) scale_acc_tuple(acc[x], alpha);
-        m_run = mn;
-      }
-      // P^T fragments: scores 8q .. 8q+7 of this lane are the k slots of step q.
-      u32x4 pf[2];
-      float lsum = 0.f;
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t pk = pack_bf16x2(exp2f(s[8 * q + 2 * d] - m_run), exp2f(s[8 * q + 2 * d + 1] - m_run));
-          pf[q][d] = pk;
-          lsum += bf16_lo(pk) + bf16_hi(pk);
-        }
-      l_run += lsum;
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head]: 16 blocks of 32 dims per
-      // k step, accumulated in AGPRs.  The wait states ahead of the first MFMA
-      // cover VALU writes of the P fragments and of a rescaled accumulator.
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        if (m + VW - 1 < 32) vf[(m + VW - 1) % VW] = load_v(m + VW - 1);
-        if (m == 0) {
-          asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[0]) : "v"(vf[0]), "v"(pf[0]));
-        } else {
-          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-              : "+a"(acc[m & 15]) : "v"(vf[m % VW]), "v"(pf[m >> 4]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = (8 * (i >> 2) + (i & 3) < rem) ? sc[i] : -INFINITY;
+        mloc = fmaxf(mloc, sc[i]);
       }
     }
+  };
+  auto sm_update = [&]() {  // running max; the 256-register rescale is deferred to all waves
+    const float mt = pair_max32(mloc) * scale_log2;
+    bool resc = false;
+    if (m_run == -INFINITY) {
+      m_run = mt;  // first tile: accumulator and sum are still zero
+    } else if (__any(mt > m_run + RESCALE_SLACK)) {
+      resc = true;
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - mn);
+      l_run *= alpha;
+      m_run = mn;
+      if (hi == 0) alpha_xchg[wave][l32] = alpha;
+    }
+    if (lane == 0) flag_xchg[wave] = resc ? 1 : 0;
+  };
+  // P^T fragments: scores 8q .. 8q+7 of this lane are the k slots of step q.
+  // Exponents are at most RESCALE_SLACK, so the hardware exp2 needs no range
+  // handling (masked keys give exp2(-inf) = 0).  The row sum adds the
+  // bf16-rounded weights that the MFMA consumes.
+  u32x4 pf[2];
+  auto sm_exp = [&](const f32x16& sc, int q, int d) {  // scores 8q + 2d, 8q + 2d + 1
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * q + 2 * d], scale_log2, -m_run));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * q + 2 * d + 1], scale_log2, -m_run));
+    const uint32_t pk = pack_bf16x2(e0, e1);
+    pf[q][d] = pk;
+    l_run = dot2_bf16_ones(pk, l_run);
+  };
+
+  // ---- tile loop ------------------------------------------------------------
+  // Pass t: QK of tile t+1 on the matrix cores while the VALU runs the softmax
+  // of tile t, then P^T exchange and PV of tile t.  Tiles t and t+1 are read
+  // from LDS during pass t, tiles t+2 and t+3 are in flight.
+  f32x16 s_cur;
+  if (ntiles > 2) wait_vmcnt<2 * DMA_PER_THREAD>();
+  else if (ntiles > 1) wait_vmcnt<DMA_PER_THREAD>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  {
+    const unsigned char* K0 = smem;
+    qk_begin(K0);
+#pragma unroll
+    for (int j = 0; j < 36; ++j) {
+      qk_step(K0, j, s_cur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (!wave_on) return;
+  for (int t = 0; t < ntiles; ++t) {
+    const bool has_next = t + 1 < ntiles;
+    // tile t+1 has landed once at most tile t+2's loads are outstanding; the
+    // barrier makes every thread's loads visible and ends every wave's use of
+    // tile t-1's stage and of the P^T and rescale slots.
+    if (t + 2 < ntiles) wait_vmcnt<DMA_PER_THREAD>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    // tile t+3 goes to the stage that held tile t-1
+    if (t + DEPTH < ntiles) {
+      issue_next(next_page);
+      if (t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
+    }
+    const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
+    const int kb = k0 + t * TILE;
+    f32x16 s_next;
+    if (has_next) {
+      const unsigned char* Kn = smem + ((t + 1) % NSTAGE) * STAGE;
+      qk_begin(Kn);
+#pragma unroll
+      for (int j = 0; j < 36; ++j) {
+        qk_step(Kn, j, s_next);
+        if (j == 1) sm_max(s_cur, kb);
+        if (j == 3) sm_update();
+        if (j >= 5 && j < 13) sm_exp(s_cur, (j - 5) >> 2, (j - 5) & 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      sm_max(s_cur, kb);
+      sm_update();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm_exp(s_cur, i >> 2, i & 3);
+    }
+    // publish this head block's P^T (exactly the B operand layout of the PV product)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) p_xchg[(wave * 2 + q) * 64 + lane] = pf[q];
+    __syncthreads();
+
+    // ---- rescale the accumulator columns of head blocks whose max was raised
+    uint32_t flags;  // byte hb = flag of head block hb, read in one LDS access
+    __builtin_memcpy(&flags, flag_xchg, 4);
+    flags = __builtin_amdgcn_readfirstlane(flags);
+    if (flags) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        if ((flags >> (8 * hb)) & 1) {
+          const float al = alpha_xchg[hb][l32];
+          asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+          for (int d = 0; d < 4; ++d) scale_acc_tuple(acc[4 * d + hb], al);
+          asm volatile("s_nop 4" ::: "memory");
+        }
+      }
+    }
+
+    // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head] for this wave's 128
+    // dims and all 128 heads: per k step q, 4 dim blocks x 4 head blocks.
+    constexpr int VW = 3;  // V fragments in flight
+    auto load_v = [&](int m) {  // fragment m: k step m >> 2, dim block 4 * wave + (m & 3)
+      const int q = m >> 2, d = m & 3;
+      const unsigned char* Kd = Kc + 256 * wave + 128 * (d >> 1);
+      const u32x2 lo = lds_tr16(Kd + pv_off[q][0][d & 1]);
+      const u32x2 hv = lds_tr16(Kd + pv_off[q][1][d & 1]);
+      return u32x4{lo[0], lo[1], hv[0], hv[1]};
+    };
+    u32x4 vf[VW];
+#pragma unroll
+    for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      u32x4 pb[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) pb[hb] = p_xchg[(hb * 2 + q) * 64 + lane];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int m = 4 * q + d;
+        if (m + VW - 1 < 8) vf[(m + VW - 1) % VW] = load_v(m + VW - 1);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          if (m == 0 && hb == 0) {
+            asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
+          } else {
+            asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (has_next) s_cur = s_next;
+  }
   // wait states before VALU reads of accumulators last written by an MFMA
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
                  "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
                  "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
 
+  if (bad_page && tid == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
+  // Each head block's owner publishes its softmax sums (and writes m, l of a split).
   const float l_tot = pair_sum32(l_run);
-  const int head = head0 + l32;
-  if (head >= a.H) return;
-  // normalised by this chunk's sum: the final output when the row is one
-  // chunk, else a partial the merge combines with weights 2^(m - m*) * l
-  const float inv = 1.f / l_tot;
-  bf16* o = (n_split_row == 1 ? (bf16*)a.o_lat + (qrow * a.H + head) * DC
-                              : (bf16*)a.part_o + ((int64_t)w * a.H + head) * DC) + 4 * hi;
-#pragma unroll
-  for (int blk = 0; blk < 16; ++blk)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 v;
-      v[0] = pack_bf16x2(acc[blk][4 * q4] * inv, acc[blk][4 * q4 + 1] * inv);
-      v[1] = pack_bf16x2(acc[blk][4 * q4 + 2] * inv, acc[blk][4 * q4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(o + 32 * blk + 8 * q4) = v;
-    }
-  if (n_split_row > 1 && hi == 0) {
-    const int64_t slot = (int64_t)w * a.H + head;
+  if (hi == 0) lsum_xchg[wave][l32] = l_tot;
+  if (multi && hi == 0 && head0 + l32 < a.H) {
+    const int64_t slot = (int64_t)w * a.H + head0 + l32;
     a.part_ml[slot * 2] = m_run;
     a.part_ml[slot * 2 + 1] = l_tot;
+  }
+  __syncthreads();
+  // normalised by this chunk's sum: the final output when the row is one
+  // chunk, else a partial the merge combines with weights 2^(m - m*) * l.
+  // Lane (l32, hi), tuple (d, hb), register 4g + e holds dim
+  // 128 wave + 32 d + 8 g + 4 hi + e of head 128 hg + 32 hb + l32.
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = hg * WG_HEADS + 32 * hb + l32;
+    if (head >= a.H) break;
+    const float inv = 1.f / lsum_xchg[hb][l32];
+    bf16* o = (!multi ? (bf16*)a.o_lat + (qrow * a.H + head) * DC
+                                : (bf16*)a.part_o + ((int64_t)w * a.H + head) * DC) + 128 * wave + 4 * hi;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& t = acc[4 * d + hb];
+        u32x2 v;
+        v[0] = pack_bf16x2(t[4 * g] * inv, t[4 * g + 1] * inv);
+        v[1] = pack_bf16x2(t[4 * g + 2] * inv, t[4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(o + 32 * d + 8 * g) = v;
+      }
   }
 }
 
@@ -489,6 +596,22 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
     plan[2 + n_rows] = carry;
     plan[0] = carry;
   }
+  __syncthreads();
+  // Per-workgroup item table in launch order (each thread re-reads only the
+  // row offsets it wrote itself).
+  const int n_items = carry;
+  int4* info = reinterpret_cast<int4*>(plan + plan_info_offset(n_rows));
+  for (int r = tid; r < n_rows; r += 1024) {
+    const int v = vis(r);
+    const int c = (v + chunk - 1) / chunk;
+    const int first = plan[2 + r];
+    for (int i = 0; i < c; ++i) {
+      const int item = first + i;
+      const int slot = a.longest_first ? n_items - 1 - item : item;
+      info[slot] = make_int4(r, i * chunk, min((i + 1) * chunk, v), (item << 1) | (c > 1 ? 1 : 0));
+    }
+  }
+  for (int i = n_items + tid; i < a.max_items; i += 1024) info[i] = make_int4(0, 0, 0, 0);
 }
 
 // fp32 reference-shape kernel: one workgroup per (query row, head), any d_c

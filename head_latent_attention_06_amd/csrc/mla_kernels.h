@@ -12,7 +12,15 @@ namespace mla {
 // chunks of `chunk` keys; each (chunk, head group of 128) is one workgroup.
 //
 // Plan layout (int32, device): [0] n_items, [1] chunk, [2 + r] first item of
-// row r for r = 0 .. n_rows (row r owns items plan[2+r] .. plan[3+r]-1).
+// row r for r = 0 .. n_rows (row r owns items plan[2+r] .. plan[3+r]-1), then
+// from plan_info_offset(n_rows) one int4 per workgroup of the attention grid,
+// in launch order: {row, first key, end key, item << 1 | row has several items};
+// entries past the last item have first key == end key.
+__host__ __device__ inline int64_t plan_info_offset(int64_t n_rows) { return (n_rows + 3 + 3) / 4 * 4; }
+__host__ __device__ inline int64_t plan_ints(int64_t n_rows, int64_t max_items) {
+  return plan_info_offset(n_rows) + 4 * max_items;
+}
+
 struct AttnArgs {
   const void* q_lat;          // [n_rows, H, ld_q]: first d_c = W_i^UK^T q^C_i
   const void* q_rope;         // [n_rows, H, ld_r]: first d_rope = q^R_i (rotated)
