@@ -71,7 +71,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t max_plan_items(const mla_config* c, int64_t n_rows, int32_t max_kv, int32_t target) {
   const int64_t by_cap = n_rows * ceil_div(max_kv, max_chunk_keys(c));
   const int64_t by_target = target > 0 ? n_rows + (int64_t)target * RAGGED_FACTOR : 0;
-  return by_target > by_cap ? by_target : by_cap;
+  const int64_t m = by_target > by_cap ? by_target : by_cap;
+  // the attention grid spreads the items over the 8 XCDs in equal runs, which
+  // can leave up to 7 empty slots: round up to whole rounds of 8
+  return m > 0 ? (m + 7 + 7) / 8 * 8 : 0;
 }
 
 // ----- workspace layouts --------------------------------------------------

@@ -267,7 +267,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- per-tile pieces ----------------------------------------------------
   // S^T[key][head] for the 32 keys of a tile and this wave's 32 heads, in
   // VGPRs: 36 MFMAs over the 576 dims.  K fragments are read KW steps ahead.
-  constexpr int KW = 3;
+  constexpr int KW = 5;
   u32x4 kf[KW];
   auto qk_begin = [&](const unsigned char* K) {
 #pragma unroll
@@ -361,11 +361,12 @@ void attn_bf16_kernel(AttnArgs a) {
     if (t + 2 < ntiles) wait_vmcnt<DMA_PER_THREAD>();
     else wait_vmcnt<0>();
     __syncthreads();
-    // tile t+3 goes to the stage that held tile t-1
-    if (t + DEPTH < ntiles) {
-      issue_next(next_page);
-      if (t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
-    }
+    // tile t+3 goes to the stage that held tile t-1; its loads are spread over
+    // this pass's PV MFMAs (all waves issuing at once would queue on the
+    // CU's address unit)
+    const bool do_issue = t + DEPTH < ntiles;
+    TileDma nd;
+    if (do_issue) nd = prep_tile(next_page);
     const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
     const int kb = k0 + t * TILE;
     f32x16 s_next;
@@ -386,10 +387,28 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sm_exp(s_cur, i >> 2, i & 3);
     }
+    if (do_issue && t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
     // publish this head block's P^T (exactly the B operand layout of the PV product)
 #pragma unroll
     for (int q = 0; q < 2; ++q) p_xchg[(wave * 2 + q) * 64 + lane] = pf[q];
     __syncthreads();
+
+    // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head] for this wave's 128
+    // dims and all 128 heads: per k step q, 4 dim blocks x 4 head blocks.
+    constexpr int VW = 3;  // V fragments in flight
+    auto load_v = [&](int m) {  // fragment m: k step m >> 2, dim block 4 * wave + (m & 3)
+      const int q = m >> 2, d = m & 3;
+      const unsigned char* Kd = Kc + 256 * wave + 128 * (d >> 1);
+      const u32x2 lo = lds_tr16(Kd + pv_off[q][0][d & 1]);
+      const u32x2 hv = lds_tr16(Kd + pv_off[q][1][d & 1]);
+      return u32x4{lo[0], lo[1], hv[0], hv[1]};
+    };
+    u32x4 pb[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) pb[0][hb] = p_xchg[hb * 2 * 64 + lane];
+    u32x4 vf[VW];
+#pragma unroll
+    for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
 
     // ---- rescale the accumulator columns of head blocks whose max was raised
     uint32_t flags;  // byte hb = flag of head block hb, read in one LDS access
@@ -408,37 +427,29 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
 
-    // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head] for this wave's 128
-    // dims and all 128 heads: per k step q, 4 dim blocks x 4 head blocks.
-    constexpr int VW = 3;  // V fragments in flight
-    auto load_v = [&](int m) {  // fragment m: k step m >> 2, dim block 4 * wave + (m & 3)
-      const int q = m >> 2, d = m & 3;
-      const unsigned char* Kd = Kc + 256 * wave + 128 * (d >> 1);
-      const u32x2 lo = lds_tr16(Kd + pv_off[q][0][d & 1]);
-      const u32x2 hv = lds_tr16(Kd + pv_off[q][1][d & 1]);
-      return u32x4{lo[0], lo[1], hv[0], hv[1]};
-    };
-    u32x4 vf[VW];
-#pragma unroll
-    for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      u32x4 pb[4];
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pb[hb] = p_xchg[(hb * 2 + q) * 64 + lane];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int m = 4 * q + d;
         if (m + VW - 1 < 8) vf[(m + VW - 1) % VW] = load_v(m + VW - 1);
+        if (q == 0 && d == 1) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) pb[1][hb] = p_xchg[(hb * 2 + 1) * 64 + lane];
+        }
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
           if (m == 0 && hb == 0) {
             asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[q][hb]));
           } else {
             asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[q][hb]));
           }
+          // one of tile t+3's loads after every third MFMA
+          const int mi = 4 * m + hb;
+          if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD && do_issue)
+            dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -452,36 +463,50 @@ void attn_bf16_kernel(AttnArgs a) {
                  "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
 
   if (bad_page && tid == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
-  // Each head block's owner publishes its softmax sums (and writes m, l of a split).
+  // Each head block's owner publishes its softmax sums.
   const float l_tot = pair_sum32(l_run);
   if (hi == 0) lsum_xchg[wave][l32] = l_tot;
-  if (multi && hi == 0 && head0 + l32 < a.H) {
-    const int64_t slot = (int64_t)w * a.H + head0 + l32;
-    a.part_ml[slot * 2] = m_run;
-    a.part_ml[slot * 2 + 1] = l_tot;
-  }
   __syncthreads();
   // normalised by this chunk's sum: the final output when the row is one
   // chunk, else a partial the merge combines with weights 2^(m - m*) * l.
   // Lane (l32, hi), tuple (d, hb), register 4g + e holds dim
-  // 128 wave + 32 d + 8 g + 4 hi + e of head 128 hg + 32 hb + l32.
+  // 128 wave + 32 d + 8 g + 4 hi + e of head 128 hg + 32 hb + l32.  Lanes l
+  // and l + 32 trade halves (v_permlane32_swap: lanes 32..63 of the first
+  // operand with lanes 0..31 of the second) so each stores 8 whole dims.
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int head = hg * WG_HEADS + 32 * hb + l32;
     if (head >= a.H) break;
     const float inv = 1.f / lsum_xchg[hb][l32];
     bf16* o = (!multi ? (bf16*)a.o_lat + (qrow * a.H + head) * DC
-                                : (bf16*)a.part_o + ((int64_t)w * a.H + head) * DC) + 128 * wave + 4 * hi;
+                      : (bf16*)a.part_o + ((int64_t)w * a.H + head) * DC) + 128 * wave;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gp = 0; gp < 2; ++gp) {  // dim groups g0 = 2 gp, g1 = 2 gp + 1
         const f32x16& t = acc[4 * d + hb];
-        u32x2 v;
-        v[0] = pack_bf16x2(t[4 * g] * inv, t[4 * g + 1] * inv);
-        v[1] = pack_bf16x2(t[4 * g + 2] * inv, t[4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(o + 32 * d + 8 * g) = v;
+        uint32_t own[2][2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int g = 2 * gp + k;
+          own[k][0] = pack_bf16x2(t[4 * g] * inv, t[4 * g + 1] * inv);
+          own[k][1] = pack_bf16x2(t[4 * g + 2] * inv, t[4 * g + 3] * inv);
+        }
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(own[0][e], own[1][e], false, false);
+          v[e] = r[0];
+          v[2 + e] = r[1];
+        }
+        // lane hi = 0 now holds dims 8 g0 .. 8 g0 + 7, lane hi = 1 dims 8 g1 .. 8 g1 + 7
+        *reinterpret_cast<u32x4*>(o + 32 * d + 8 * (2 * gp + hi)) = v;
       }
+  }
+  if (multi && hi == 0 && head0 + l32 < a.H) {
+    const int64_t slot = (int64_t)w * a.H + head0 + l32;
+    a.part_ml[slot * 2] = m_run;
+    a.part_ml[slot * 2 + 1] = l_tot;
   }
 }
 
@@ -599,7 +624,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
   __syncthreads();
   // Per-workgroup item table in launch order (each thread re-reads only the
   // row offsets it wrote itself).
+  // Launch order: workgroup i runs on XCD i % 8.  Without longest_first the
+  // items go to the XCDs in 8 runs of consecutive items, so the chunks of one
+  // row (which read the same queries) share an L2; with longest_first the items
+  // run in reverse plan order.  The grid has at least n_items + 7 slots.
   const int n_items = carry;
+  const int per = (n_items + 7) / 8;
   int4* info = reinterpret_cast<int4*>(plan + plan_info_offset(n_rows));
   for (int r = tid; r < n_rows; r += 1024) {
     const int v = vis(r);
@@ -607,11 +637,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
     const int first = plan[2 + r];
     for (int i = 0; i < c; ++i) {
       const int item = first + i;
-      const int slot = a.longest_first ? n_items - 1 - item : item;
+      const int slot = a.longest_first ? n_items - 1 - item : (item % per) * 8 + item / per;
       info[slot] = make_int4(r, i * chunk, min((i + 1) * chunk, v), (item << 1) | (c > 1 ? 1 : 0));
     }
   }
-  for (int i = n_items + tid; i < a.max_items; i += 1024) info[i] = make_int4(0, 0, 0, 0);
+  for (int s = tid; s < a.max_items; s += 1024) {
+    const bool used = a.longest_first ? s < n_items : (s / 8 < per && (s % 8) * per + s / 8 < n_items);
+    if (!used) info[s] = make_int4(0, 0, 0, 0);
+  }
 }
 
 // fp32 reference-shape kernel: one workgroup per (query row, head), any d_c
