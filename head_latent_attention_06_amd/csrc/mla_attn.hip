@@ -267,7 +267,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- per-tile pieces ----------------------------------------------------
   // S^T[key][head] for the 32 keys of a tile and this wave's 32 heads, in
   // VGPRs: 36 MFMAs over the 576 dims.  K fragments are read KW steps ahead.
-  constexpr int KW = 5;
+  constexpr int KW = 4;
   u32x4 kf[KW];
   auto qk_begin = [&](const unsigned char* K) {
 #pragma unroll
@@ -288,51 +288,77 @@ void attn_bf16_kernel(AttnArgs a) {
           : "+v"(sacc) : "v"(kf[j % KW]), "v"(qf[j]));
     }
   };
-  // Online softmax (log2 domain) of one tile for this wave's heads, in three
-  // stages so it can run between the next tile's QK MFMAs.  Lane holds keys
-  // kb + 8*(i/4) + 4*hi + i%4 of head l32.  The scale is positive, so the max
-  // is taken on raw scores and the scale folded into the exponent's FMA.
-  float mloc;
-  auto sm_max = [&](f32x16& sc, int kb) {
-    mloc = -INFINITY;
-    if (kb + TILE <= k1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
-    } else {
-      const int rem = k1 - kb - 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sc[i] = (8 * (i >> 2) + (i & 3) < rem) ? sc[i] : -INFINITY;
-        mloc = fmaxf(mloc, sc[i]);
-      }
-    }
-  };
-  auto sm_update = [&]() {  // running max; the 256-register rescale is deferred to all waves
-    const float mt = pair_max32(mloc) * scale_log2;
-    bool resc = false;
-    if (m_run == -INFINITY) {
-      m_run = mt;  // first tile: accumulator and sum are still zero
-    } else if (__any(mt > m_run + RESCALE_SLACK)) {
-      resc = true;
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - mn);
-      l_run *= alpha;
-      m_run = mn;
-      if (hi == 0) alpha_xchg[wave][l32] = alpha;
-    }
-    if (lane == 0) flag_xchg[wave] = resc ? 1 : 0;
-  };
-  // P^T fragments: scores 8q .. 8q+7 of this lane are the k slots of step q.
-  // Exponents are at most RESCALE_SLACK, so the hardware exp2 needs no range
-  // handling (masked keys give exp2(-inf) = 0).  The row sum adds the
-  // bf16-rounded weights that the MFMA consumes.
+  // Online softmax (log2 domain) of one tile for this wave's heads, cut into
+  // slots that run between the next tile's QK MFMAs.  No instruction in a slot
+  // depends on another of the same slot (a dependent chain would hold up the
+  // in-order issue of the next MFMA).  Lane holds keys kb + 8*(i/4) + 4*hi + i%4
+  // of head l32.  The scale is positive, so the max is taken on raw scores and
+  // the scale folded into the exponent's FMA.
+  constexpr int SM_SLOTS = 27;
+  float mx0, mx1, neg_m;
+  float ex[16];
   u32x4 pf[2];
-  auto sm_exp = [&](const f32x16& sc, int q, int d) {  // scores 8q + 2d, 8q + 2d + 1
-    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * q + 2 * d], scale_log2, -m_run));
-    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * q + 2 * d + 1], scale_log2, -m_run));
-    const uint32_t pk = pack_bf16x2(e0, e1);
-    pf[q][d] = pk;
-    l_run = dot2_bf16_ones(pk, l_run);
+  auto max3 = [](float x, float y, float z) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+    return r;
+  };
+  auto sm_slot = [&](int j, f32x16& sc, int kb, bool first) {
+    if (j == 1) {
+      if (kb + TILE > k1) {  // the chunk's last, partial tile
+        const int rem = k1 - kb - 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = (8 * (i >> 2) + (i & 3) < rem) ? sc[i] : -INFINITY;
+      }
+      mx0 = max3(sc[0], sc[1], sc[2]);
+      mx1 = max3(sc[3], sc[4], sc[5]);
+    } else if (j == 2) {
+      mx0 = max3(mx0, sc[6], sc[7]);
+      mx1 = max3(mx1, sc[8], sc[9]);
+    } else if (j == 3) {
+      mx0 = max3(mx0, sc[10], sc[11]);
+      mx1 = max3(mx1, sc[12], sc[13]);
+    } else if (j == 4) {
+      mx0 = max3(mx0, mx1, sc[14]);
+    } else if (j == 5) {
+      mx0 = max3(mx0, sc[15], sc[15]);
+    } else if (j == 6) {  // the other half of the head's keys sits in lane l ^ 32
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx0), false, false);
+      mx0 = __uint_as_float(r[0]);
+      mx1 = __uint_as_float(r[1]);
+    } else if (j == 7) {
+      mx0 = max3(mx0, mx1, mx1) * scale_log2;  // tile max, log2 units
+    } else if (j == 8) {
+      // running max: raised only when the tile max exceeds it by more than
+      // RESCALE_SLACK (p <= 2^8 stays exact); the accumulator rescale is done
+      // by every wave after the P^T exchange
+      bool resc = false;
+      if (first) {
+        m_run = mx0;  // accumulator and sum are still zero
+      } else if (__builtin_amdgcn_ballot_w64(mx0 > m_run + RESCALE_SLACK)) {
+        resc = true;
+        const float mn = fmaxf(m_run, mx0);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+        m_run = mn;
+        alpha_xchg[wave][l32] = alpha;  // lanes l and l ^ 32 store the same value
+      }
+      flag_xchg[wave] = resc ? 1 : 0;  // every lane stores the same byte
+      neg_m = -m_run;
+    }
+    // P^T fragments: scores 8q .. 8q+7 of this lane are the k slots of step q.
+    // Exponents are at most RESCALE_SLACK, so the hardware exp2 needs no range
+    // handling (masked keys give exp2(-inf) = 0).  Score i: FMA in slot 9 + i,
+    // exp2 in 10 + i; pair k = (2k, 2k+1) is packed and summed in slot 12 + 2k
+    // (one transcendental per slot fits under one MFMA; the row sum uses fp32
+    // adds, which overlap the MFMAs where a dot2 instruction would not).
+    if (j >= 9 && j < 25) ex[j - 9] = __builtin_fmaf(sc[j - 9], scale_log2, neg_m);
+    if (j >= 10 && j < 26) ex[j - 10] = __builtin_amdgcn_exp2f(ex[j - 10]);
+    if (j >= 12 && j < 27 && (j & 1) == 0) {
+      const int k = (j - 12) >> 1;
+      pf[k >> 2][k & 3] = pack_bf16x2(ex[2 * k], ex[2 * k + 1]);
+      l_run += ex[2 * k] + ex[2 * k + 1];
+    }
   };
 
   // ---- tile loop ------------------------------------------------------------
@@ -365,8 +391,7 @@ void attn_bf16_kernel(AttnArgs a) {
     // this pass's PV MFMAs (all waves issuing at once would queue on the
     // CU's address unit)
     const bool do_issue = t + DEPTH < ntiles;
-    TileDma nd;
-    if (do_issue) nd = prep_tile(next_page);
+    TileDma nd;  // prepared between the QK MFMAs (scalar work overlaps them)
     const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
     const int kb = k0 + t * TILE;
     f32x16 s_next;
@@ -376,16 +401,14 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 36; ++j) {
         qk_step(Kn, j, s_next);
-        if (j == 1) sm_max(s_cur, kb);
-        if (j == 3) sm_update();
-        if (j >= 5 && j < 13) sm_exp(s_cur, (j - 5) >> 2, (j - 5) & 3);
+        if (j < SM_SLOTS) sm_slot(j, s_cur, kb, t == 0);
+        if (j == SM_SLOTS + 1 && do_issue) nd = prep_tile(next_page);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      sm_max(s_cur, kb);
-      sm_update();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm_exp(s_cur, i >> 2, i & 3);
+      for (int j = 0; j < SM_SLOTS; ++j) sm_slot(j, s_cur, kb, t == 0);
+      if (do_issue) nd = prep_tile(next_page);
     }
     if (do_issue && t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
     // publish this head block's P^T (exactly the B operand layout of the PV product)
@@ -403,6 +426,8 @@ void attn_bf16_kernel(AttnArgs a) {
       const u32x2 hv = lds_tr16(Kd + pv_off[q][1][d & 1]);
       return u32x4{lo[0], lo[1], hv[0], hv[1]};
     };
+    uint32_t flags;  // byte hb = flag of head block hb, read first, in one LDS access
+    __builtin_memcpy(&flags, flag_xchg, 4);
     u32x4 pb[2][4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) pb[0][hb] = p_xchg[hb * 2 * 64 + lane];
@@ -411,8 +436,6 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
 
     // ---- rescale the accumulator columns of head blocks whose max was raised
-    uint32_t flags;  // byte hb = flag of head block hb, read in one LDS access
-    __builtin_memcpy(&flags, flag_xchg, 4);
     flags = __builtin_amdgcn_readfirstlane(flags);
     if (flags) {
 #pragma unroll

@@ -37,13 +37,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// acc + lo + hi of a packed bf16 pair (one v_dot2c_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float dot2_bf16_ones(uint32_t v, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
-                                         acc, false);
-}
-
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
