@@ -142,14 +142,36 @@ void attn_bf16_kernel(AttnArgs a) {
   const int64_t qrow = row;
   const float scale_log2 = a.scale * LOG2E;
 
-  // ---- the chunk's page ids, staged once (keeps block-table reads off the pipeline)
+  // ---- loads that do not depend on each other, issued back to back: the
+  // chunk's page ids (staged in LDS, keeping block-table reads off the tile
+  // pipeline), then the queries
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int pg_first = k0 / a.page_size;
   const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
-  for (int i = tid; i < n_pages; i += 256) {
-    const int pidx = pg_first + i;
-    split_pages[i] = pidx < a.max_pages ? bt[pidx] : -1;
+  constexpr int PAGES_PER_THREAD = MAX_SPLIT_PAGES / 256;
+  int pid[PAGES_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < PAGES_PER_THREAD; ++k) {
+    const int i = tid + 256 * k, pidx = pg_first + i;
+    pid[k] = (i < n_pages && pidx < a.max_pages) ? bt[pidx] : -1;
   }
+  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
+  // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
+  u32x4 qf[36];
+  {
+    const int nh = wave_on ? min(32, a.H - head0) : 0;
+    const int64_t hrow = qrow * a.H + (wave_on ? head0 : 0);
+    const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
+    const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
+#pragma unroll
+    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
+  }
+#pragma unroll
+  for (int k = 0; k < PAGES_PER_THREAD; ++k)
+    if (tid + 256 * k < n_pages) split_pages[tid + 256 * k] = pid[k];
   __syncthreads();
 
   // ---- tile loads: wave w's instruction i covers LDS chunks (4i + w)*64 + lane
@@ -201,23 +223,8 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   const int ntiles = (k1 - k0 + TILE - 1) / TILE;
 
-  // ---- prologue loads, in the order the first tile needs them: tile 0, the
-  // queries, then tiles 1 .. DEPTH-1 (vector loads complete in issue order).
+  // ---- tile 0 (vector loads complete in issue order: the queries, then tile 0)
   issue_next(split_pages[0]);
-  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
-  // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
-  u32x4 qf[36];
-  {
-    const int nh = wave_on ? min(32, a.H - head0) : 0;
-    const int64_t hrow = qrow * a.H + (wave_on ? head0 : 0);
-    const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
-    const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
-#pragma unroll
-    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
-  }
   // Wait for the queries (and tile 0) here: left to the compiler, the wait
   // would sit inside the tile loop in front of the MFMAs that read them and
   // would drain the tile loads in flight on every pass.
