@@ -543,61 +543,88 @@ void attn_bf16_kernel(AttnArgs a) {
 // Merge of split partials o_k = acc_k / l_k (m_k in the log2 domain):
 //   o_lat = sum_k 2^(m_k - m*) l_k o_k / sum_k 2^(m_k - m*) l_k,  m* = max_k m_k.
 // Rows cut into a single chunk were written by the attention kernel; rows
-// with no chunk (invalid length) are written as zero.
-__global__ __launch_bounds__(128) void merge_bf16_kernel(AttnArgs a) {
-  const int head = blockIdx.x % a.H;
-  const int64_t row = blockIdx.x / a.H;
-  const int t = threadIdx.x;
+// with no chunk (invalid length) are written as zero.  One workgroup per
+// (row, 4 heads): 64 threads per head, 8 dims (16 bytes) per thread; the
+// loads of up to MERGE_BATCH splits are issued together.
+constexpr int MERGE_BATCH = 8;
+__global__ __launch_bounds__(256) void merge_bf16_kernel(AttnArgs a) {
+  const int hq = a.H / 4;
+  const int64_t row = blockIdx.x / hq;
+  const int head = (int)(blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
+  const int t = threadIdx.x & 63;
   const int32_t* row_off = a.plan + 2;
   const int i0 = row_off[row], n = row_off[row + 1] - i0;
   if (n == 1) return;
-  bf16* o = (bf16*)a.o_lat + (row * a.H + head) * DC + 4 * t;
-  u32x2 outv = {0u, 0u};
+  u32x4 outv = {0u, 0u, 0u, 0u};
   if (n > 1) {
-    float mstar = -INFINITY;
-    for (int k = 0; k < n; ++k) mstar = fmaxf(mstar, a.part_ml[((int64_t)(i0 + k) * a.H + head) * 2]);
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < n; ++k) {
-      const int64_t slot = (int64_t)(i0 + k) * a.H + head;
-      const float wk = exp2f(a.part_ml[slot * 2] - mstar) * a.part_ml[slot * 2 + 1];
-      L += wk;
-      const u32x2 v = *reinterpret_cast<const u32x2*>((const bf16*)a.part_o + slot * DC + 4 * t);
-      acc[0] += wk * bf16_lo(v[0]);
-      acc[1] += wk * bf16_hi(v[0]);
-      acc[2] += wk * bf16_lo(v[1]);
-      acc[3] += wk * bf16_hi(v[1]);
+    // all (m, l) pairs and partial vectors of a batch are loaded before use
+    float mstar = -INFINITY, L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < n; k0 += MERGE_BATCH) {
+      u32x4 v[MERGE_BATCH];
+      float mk[MERGE_BATCH], lk[MERGE_BATCH];
+#pragma unroll
+      for (int k = 0; k < MERGE_BATCH; ++k) {
+        if (k0 + k < n) {
+          const int64_t slot = (int64_t)(i0 + k0 + k) * a.H + head;
+          const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+          mk[k] = ml.x;
+          lk[k] = ml.y;
+          v[k] = *reinterpret_cast<const u32x4*>((const bf16*)a.part_o + slot * DC + 8 * t);
+        }
+      }
+      // running rescale across batches (one batch for up to MERGE_BATCH splits)
+      float mb = mstar;
+#pragma unroll
+      for (int k = 0; k < MERGE_BATCH; ++k)
+        if (k0 + k < n) mb = fmaxf(mb, mk[k]);
+      const float alpha = exp2f(mstar - mb);
+      L *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+      mstar = mb;
+#pragma unroll
+      for (int k = 0; k < MERGE_BATCH; ++k) {
+        if (k0 + k < n) {
+          const float wk = exp2f(mk[k] - mstar) * lk[k];
+          L += wk;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            acc[2 * d] += wk * bf16_lo(v[k][d]);
+            acc[2 * d + 1] += wk * bf16_hi(v[k][d]);
+          }
+        }
+      }
     }
     const float inv = 1.f / L;
-    outv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    outv[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) outv[d] = pack_bf16x2(acc[2 * d] * inv, acc[2 * d + 1] * inv);
   }
-  *reinterpret_cast<u32x2*>(o) = outv;
+  *reinterpret_cast<u32x4*>((bf16*)a.o_lat + (row * a.H + head) * DC + 8 * t) = outv;
 }
 
-// Work plan: one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, int32_t target_items,
-                                                    int32_t min_chunk, int32_t max_chunk) {
-  __shared__ long long red_tot[32];
-  __shared__ int red_max[32];
-  __shared__ int scan[1024];
-  __shared__ int carry, chunk_s;
+// Work plan: one workgroup of 256 threads (wave-level scans, three barriers
+// per 256 rows).
+__global__ __launch_bounds__(256) void plan_kernel(AttnArgs a, int32_t* plan, int32_t target_items,
+                                                   int32_t min_chunk, int32_t max_chunk) {
+  __shared__ long long red_tot[4];
+  __shared__ int red_max[4], wsum[4];
+  __shared__ int chunk_s;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_rows = a.B * a.s_q;
-  auto vis = [&](int r) -> int {
+  auto vis = [&](int r, bool report) -> int {  // visible keys of query row r
     const int b = r / a.s_q, s = r % a.s_q;
     bool ok;
     const int kv = kv_len_of(a, b, ok);
     if (!ok) {
-      if (s == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_LEN);
+      if (report && s == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_LEN);
       return 0;
     }
     return kv - a.s_q + s + 1;
   };
   long long tot = 0;
   int mx = 0;
-  for (int r = tid; r < n_rows; r += 1024) {
-    const int v = vis(r);
+  for (int r = tid; r < n_rows; r += 256) {
+    const int v = vis(r, true);
     tot += v;
     mx = max(mx, v);
   }
@@ -611,12 +638,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
   }
   __syncthreads();
   if (tid == 0) {
-    long long T = 0;
-    int M = 0;
-    for (int i = 0; i < 16; ++i) {
-      T += red_tot[i];
-      M = max(M, red_max[i]);
-    }
+    const long long T = red_tot[0] + red_tot[1] + red_tot[2] + red_tot[3];
+    const int M = max(max(red_max[0], red_max[1]), max(red_max[2], red_max[3]));
     int chunk = max_chunk;
     if (target_items > 0 && T > 0) {
       // ragged batches get four times as many, smaller, chunks to even out
@@ -626,43 +649,43 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
     }
     plan[1] = chunk;
     chunk_s = chunk;
-    carry = 0;
   }
   __syncthreads();
   const int chunk = chunk_s;
-  for (int base = 0; base < n_rows; base += 1024) {
+  // exclusive scan of the per-row chunk counts (first item of each row)
+  int carry = 0;
+  for (int base = 0; base < n_rows; base += 256) {
     const int r = base + tid;
-    const int v = r < n_rows ? vis(r) : 0;
-    const int c = (v + chunk - 1) / chunk;
-    scan[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-      const int x = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += x;
-      __syncthreads();
+    const int c = r < n_rows ? (vis(r, false) + chunk - 1) / chunk : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
     }
-    if (r < n_rows) plan[2 + r] = carry + scan[tid] - c;
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    if (tid == 1023) carry += scan[1023];
+    int before = carry;
+    for (int w2 = 0; w2 < wv; ++w2) before += wsum[w2];
+    if (r < n_rows) plan[2 + r] = before + incl - c;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
   if (tid == 0) {
     plan[2 + n_rows] = carry;
     plan[0] = carry;
   }
-  __syncthreads();
   // Per-workgroup item table in launch order (each thread re-reads only the
-  // row offsets it wrote itself).
-  // Launch order: workgroup i runs on XCD i % 8.  Without longest_first the
-  // items go to the XCDs in 8 runs of consecutive items, so the chunks of one
-  // row (which read the same queries) share an L2; with longest_first the items
-  // run in reverse plan order.  The grid has at least n_items + 7 slots.
+  // row offsets it wrote itself).  Workgroup i runs on XCD i % 8.  Without
+  // longest_first the items go to the XCDs in 8 runs of consecutive items, so
+  // the chunks of one row (which read the same queries) share an L2; with
+  // longest_first the items run in reverse plan order.  The grid has at least
+  // n_items + 7 slots.
   const int n_items = carry;
   const int per = (n_items + 7) / 8;
   int4* info = reinterpret_cast<int4*>(plan + plan_info_offset(n_rows));
-  for (int r = tid; r < n_rows; r += 1024) {
-    const int v = vis(r);
+  for (int r = tid; r < n_rows; r += 256) {
+    const int v = vis(r, false);
     const int c = (v + chunk - 1) / chunk;
     const int first = plan[2 + r];
     for (int i = 0; i < c; ++i) {
@@ -671,9 +694,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a, int32_t* plan, i
       info[slot] = make_int4(r, i * chunk, min((i + 1) * chunk, v), (item << 1) | (c > 1 ? 1 : 0));
     }
   }
-  for (int s = tid; s < a.max_items; s += 1024) {
-    const bool used = a.longest_first ? s < n_items : (s / 8 < per && (s % 8) * per + s / 8 < n_items);
-    if (!used) info[s] = make_int4(0, 0, 0, 0);
+  for (int s2 = tid; s2 < a.max_items; s2 += 256) {
+    const bool used = a.longest_first ? s2 < n_items : (s2 / 8 < per && (s2 % 8) * per + s2 / 8 < n_items);
+    if (!used) info[s2] = make_int4(0, 0, 0, 0);
   }
 }
 
@@ -770,15 +793,15 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_merge_bf16(const AttnArgs& a, hipStream_t st) {
-  const int64_t n = (int64_t)a.B * a.s_q * a.H;
+  const int64_t n = (int64_t)a.B * a.s_q * (a.H / 4);  // H is a multiple of 32 on this path
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)n), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_plan(const AttnArgs& a, int32_t* plan, int32_t target_items, int32_t min_chunk,
                             int32_t max_chunk, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a, plan, target_items, min_chunk, max_chunk);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, a, plan, target_items, min_chunk, max_chunk);
   return hipGetLastError();
 }
 

@@ -227,10 +227,130 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if (m < g.M && n < g.N) ((float*)g.C)[z * g.strideC + (int64_t)m * g.ldc + n] = accv;
 }
 
+
+// ---------------------------------------------------------------------------
+// Small-M batched GEMM (decode: M = query rows <= 64 per head, K <= 512): one
+// workgroup per (64-column block, batch entry) holds the whole K extent of
+// its A and B tiles in LDS, so it makes one round of loads instead of a
+// pipeline of K slices, and the many small workgroups keep enough loads in
+// flight.  Four waves in a 2 x 2 arrangement of 32 x 32 MFMA tiles.  The
+// output tile is staged in LDS and written with 16-byte stores.
+constexpr int SM_BM = 64, SM_BN = 64;
+
+template <bool B_KN, int KMAX>
+__global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g) {
+  constexpr int RS = KMAX * 2 + 16;  // LDS row stride in bytes (16-byte pad: conflict-free fragment reads)
+  __shared__ __attribute__((aligned(16))) unsigned char sa[SM_BM * RS];
+  __shared__ __attribute__((aligned(16))) unsigned char sb[SM_BN * RS];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  // grid (batch, column blocks): consecutive workgroups (which the dispatcher
+  // deals round-robin to the XCDs) take different batch entries, so the column
+  // blocks of one batch entry share an XCD and its L2 copy of the A tile
+  const int n0 = blockIdx.y * SM_BN, z = blockIdx.x;
+  const int K = g.K, kc = K / 8;  // 16-byte chunks per row
+  const bf16* A = (const bf16*)g.A + z * g.strideA;
+  const bf16* B = (const bf16*)g.B + z * g.strideB;
+
+  // All loads are issued before any LDS store so they are in flight together.
+  constexpr int PER = SM_BM * (KMAX / 8) / 256;  // 16-byte chunks per thread and operand
+  // A rows past M load as zero
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (int64_t)(g.M - 1) * g.lda * 2 + K * 2);
+  u32x4 va[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i, r = c / kc, k8 = c % kc;
+    if (c < SM_BM * kc) va[i] = bld16(ra, (int32_t)((int64_t)r * g.lda * 2 + k8 * 16));
+  }
+  if (!B_KN) {  // B given [N, K]: rows of the column block
+    const int rows = min(SM_BN, g.N - n0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(B + (int64_t)n0 * g.ldb, (int64_t)(rows - 1) * g.ldb * 2 + K * 2);
+    u32x4 vb[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i, r = c / kc, k8 = c % kc;
+      if (c < SM_BN * kc) vb[i] = bld16(rb, (int32_t)((int64_t)r * g.ldb * 2 + k8 * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i, r = c / kc, k8 = c % kc;
+      if (c < SM_BN * kc) *(u32x4*)(sb + r * RS + k8 * 16) = vb[i];
+    }
+  } else {  // B given [K, N]: 8 x 8 blocks transposed in registers to [n][k]
+    const __amdgpu_buffer_rsrc_t rb = rsrc(B + n0, (int64_t)(K - 1) * g.ldb * 2 + (int64_t)min(SM_BN, g.N - n0) * 2);
+    constexpr int BPER = ((KMAX / 8) * (SM_BN / 8) + 255) / 256;  // 8 x 8 blocks per thread
+    u32x4 in[BPER][8];
+#pragma unroll
+    for (int q = 0; q < BPER; ++q) {
+      const int blk = tid + 256 * q, kb = blk / (SM_BN / 8), nb = blk % (SM_BN / 8);
+      if (blk < kc * (SM_BN / 8)) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) in[q][r] = bld16(rb, (int32_t)((int64_t)(8 * kb + r) * g.ldb * 2 + nb * 16));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < BPER; ++q) {
+      const int blk = tid + 256 * q, kb = blk / (SM_BN / 8), nb = blk % (SM_BN / 8);
+      if (blk < kc * (SM_BN / 8)) {
+        u32x4 out[8];
+        transpose8x8(in[q], out);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) *(u32x4*)(sb + (8 * nb + c) * RS + kb * 16) = out[c];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i, r = c / kc, k8 = c % kc;
+    if (c < SM_BM * kc) *(u32x4*)(sa + r * RS + k8 * 16) = va[i];
+  }
+  __syncthreads();
+
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const unsigned char* pa = sa + (32 * wm + l32) * RS + 16 * hi;
+  const unsigned char* pb = sb + (32 * wn + l32) * RS + 16 * hi;
+#pragma unroll 8
+  for (int s = 0; s < K / 16; ++s) acc = mfma32(*(const u32x4*)(pa + 32 * s), *(const u32x4*)(pb + 32 * s), acc);
+  __syncthreads();  // the A tile's LDS is reused for the output tile
+
+  // lane l, register i: row 32 wm + 8 (i/4) + 4 hi + i%4, column 32 wn + l32
+  constexpr int CS = SM_BN * 2 + 16;
+  bf16* sc = (bf16*)sa;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    sc[(32 * wm + 8 * (i >> 2) + 4 * hi + (i & 3)) * (CS / 2) + 32 * wn + l32] = (bf16)acc[i];
+  __syncthreads();
+  bf16* C = (bf16*)g.C + z * g.strideC;
+  for (int c = tid; c < SM_BM * (SM_BN / 8); c += 256) {
+    const int r = c / (SM_BN / 8), c8 = c % (SM_BN / 8);
+    if (r < g.M && n0 + 8 * c8 < g.N)
+      *(u32x4*)(C + (int64_t)r * g.ldc + n0 + 8 * c8) = *(const u32x4*)(sa + r * CS + c8 * 16);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  if (g.M <= SM_BM && g.K <= 512 && g.K % 64 == 0 && g.N % 8 == 0 && g.out_bf16 && !g.B2) {
+    dim3 grid((unsigned)g.batch, (unsigned)((g.N + SM_BN - 1) / SM_BN));
+    if (g.K <= 128) {
+      if (g.b_kn)
+        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 128>), grid, dim3(256), 0, st, g);
+      else
+        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 128>), grid, dim3(256), 0, st, g);
+    } else {
+      if (g.b_kn)
+        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 512>), grid, dim3(256), 0, st, g);
+      else
+        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 512>), grid, dim3(256), 0, st, g);
+    }
+    return hipGetLastError();
+  }
   const unsigned tiles = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles, (unsigned)g.batch);
   if (g.b_kn) {
