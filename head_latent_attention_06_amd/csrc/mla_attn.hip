@@ -302,7 +302,8 @@ void attn_bf16_kernel(AttnArgs a) {
   // of head l32.  The scale is positive, so the max is taken on raw scores and
   // the scale folded into the exponent's FMA.
   constexpr int SM_SLOTS = 27;
-  float mx0, mx1, neg_m;
+  float mx0, mx1, neg_m, alpha = 1.f;
+  bool resc = false;  // this tile raised the running max (published with P^T)
   float ex[16];
   u32x4 pf[2];
   auto max3 = [](float x, float y, float z) {
@@ -339,18 +340,16 @@ void attn_bf16_kernel(AttnArgs a) {
       // running max: raised only when the tile max exceeds it by more than
       // RESCALE_SLACK (p <= 2^8 stays exact); the accumulator rescale is done
       // by every wave after the P^T exchange
-      bool resc = false;
+      resc = false;
       if (first) {
         m_run = mx0;  // accumulator and sum are still zero
       } else if (__builtin_amdgcn_ballot_w64(mx0 > m_run + RESCALE_SLACK)) {
         resc = true;
         const float mn = fmaxf(m_run, mx0);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        alpha = __builtin_amdgcn_exp2f(m_run - mn);
         l_run *= alpha;
         m_run = mn;
-        alpha_xchg[wave][l32] = alpha;  // lanes l and l ^ 32 store the same value
       }
-      flag_xchg[wave] = resc ? 1 : 0;  // every lane stores the same byte
       neg_m = -m_run;
     }
     // P^T fragments: scores 8q .. 8q+7 of this lane are the k slots of step q.
@@ -369,10 +368,18 @@ void attn_bf16_kernel(AttnArgs a) {
   };
 
   // ---- tile loop ------------------------------------------------------------
-  // Pass t: QK of tile t+1 on the matrix cores while the VALU runs the softmax
-  // of tile t, then P^T exchange and PV of tile t.  Tiles t and t+1 are read
-  // from LDS during pass t, tiles t+2 and t+3 are in flight.
-  f32x16 s_cur;
+  // Pass t: QK of tile t+1 (LDS-bound: four waves read every key fragment),
+  // then PV of tile t (MFMA-bound) with the softmax of tile t+1 running
+  // between its MFMAs; tile t+1's P^T is published after the second barrier.
+  // Tiles t and t+1 are read from LDS during pass t, tiles t+2 and t+3 are in
+  // flight.
+  auto publish = [&]() {  // P^T, rescale flag and factor of this wave's head block
+#pragma unroll
+    for (int q = 0; q < 2; ++q) p_xchg[(wave * 2 + q) * 64 + lane] = pf[q];
+    if (resc) alpha_xchg[wave][l32] = alpha;  // lanes l and l ^ 32 store the same value
+    flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
+  };
+  f32x16 s_nx;  // scores of the next tile
   if (ntiles > 2) wait_vmcnt<2 * DMA_PER_THREAD>();
   else if (ntiles > 1) wait_vmcnt<DMA_PER_THREAD>();
   else wait_vmcnt<0>();
@@ -382,46 +389,38 @@ void attn_bf16_kernel(AttnArgs a) {
     qk_begin(K0);
 #pragma unroll
     for (int j = 0; j < 36; ++j) {
-      qk_step(K0, j, s_cur);
+      qk_step(K0, j, s_nx);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < SM_SLOTS; ++j) sm_slot(j, s_nx, k0, true);
+    publish();
   }
   for (int t = 0; t < ntiles; ++t) {
     const bool has_next = t + 1 < ntiles;
     // tile t+1 has landed once at most tile t+2's loads are outstanding; the
-    // barrier makes every thread's loads visible and ends every wave's use of
-    // tile t-1's stage and of the P^T and rescale slots.
+    // barrier makes every thread's loads and tile t's P^T visible
     if (t + 2 < ntiles) wait_vmcnt<DMA_PER_THREAD>();
     else wait_vmcnt<0>();
     __syncthreads();
-    // tile t+3 goes to the stage that held tile t-1; its loads are spread over
-    // this pass's PV MFMAs (all waves issuing at once would queue on the
-    // CU's address unit)
+    // tile t+3 goes to the stage that held tile t-1 (read by the previous
+    // pass); its loads are spread over this pass's PV MFMAs (all waves issuing
+    // at once would queue on the CU's address unit)
     const bool do_issue = t + DEPTH < ntiles;
-    TileDma nd;  // prepared between the QK MFMAs (scalar work overlaps them)
+    TileDma nd;
+    if (do_issue) nd = prep_tile(next_page);
     const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
-    const int kb = k0 + t * TILE;
-    f32x16 s_next;
+    const int kb_next = k0 + (t + 1) * TILE;
     if (has_next) {
       const unsigned char* Kn = smem + ((t + 1) % NSTAGE) * STAGE;
       qk_begin(Kn);
 #pragma unroll
       for (int j = 0; j < 36; ++j) {
-        qk_step(Kn, j, s_next);
-        if (j < SM_SLOTS) sm_slot(j, s_cur, kb, t == 0);
-        if (j == SM_SLOTS + 1 && do_issue) nd = prep_tile(next_page);
+        qk_step(Kn, j, s_nx);
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < SM_SLOTS; ++j) sm_slot(j, s_cur, kb, t == 0);
-      if (do_issue) nd = prep_tile(next_page);
     }
     if (do_issue && t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
-    // publish this head block's P^T (exactly the B operand layout of the PV product)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) p_xchg[(wave * 2 + q) * 64 + lane] = pf[q];
-    __syncthreads();
 
     // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head] for this wave's 128
     // dims and all 128 heads: per k step q, 4 dim blocks x 4 head blocks.
@@ -435,9 +434,9 @@ void attn_bf16_kernel(AttnArgs a) {
     };
     uint32_t flags;  // byte hb = flag of head block hb, read first, in one LDS access
     __builtin_memcpy(&flags, flag_xchg, 4);
-    u32x4 pb[2][4];
+    u32x4 pb[4];  // P^T fragments of the current k step; step 1 reloads them in place
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pb[0][hb] = p_xchg[hb * 2 * 64 + lane];
+    for (int hb = 0; hb < 4; ++hb) pb[hb] = p_xchg[hb * 2 * 64 + lane];
     u32x4 vf[VW];
 #pragma unroll
     for (int i = 0; i < VW - 1; ++i) vf[i] = load_v(i);
@@ -463,28 +462,30 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int d = 0; d < 4; ++d) {
         const int m = 4 * q + d;
         if (m + VW - 1 < 8) vf[(m + VW - 1) % VW] = load_v(m + VW - 1);
-        if (q == 0 && d == 1) {
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) pb[1][hb] = p_xchg[(hb * 2 + 1) * 64 + lane];
-        }
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
           if (m == 0 && hb == 0) {
             asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[q][hb]));
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
           } else {
             asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[q][hb]));
+                : "+a"(acc[4 * d + hb]) : "v"(vf[m % VW]), "v"(pb[hb]));
           }
-          // one of tile t+3's loads after every third MFMA
+          // after its last use in step 0, the fragment is reloaded for step 1
+          if (q == 0 && d == 3) pb[hb] = p_xchg[(hb * 2 + 1) * 64 + lane];
           const int mi = 4 * m + hb;
+          // the next tile's softmax, one slot per MFMA
+          if (has_next && mi < SM_SLOTS) sm_slot(mi, s_nx, kb_next, false);
+          // one of tile t+3's loads after every third MFMA
           if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD && do_issue)
             dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    if (has_next) s_cur = s_next;
+    // every wave is done with tile t's P^T and rescale slots
+    __syncthreads();
+    if (has_next) publish();
   }
   // wait states before VALU reads of accumulators last written by an MFMA
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
