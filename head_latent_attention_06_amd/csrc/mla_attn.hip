@@ -54,6 +54,11 @@ constexpr int FLAG_BAD_PAGE = 1, FLAG_BAD_LEN = 4;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.0f;
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 __device__ __forceinline__ int kv_len_of(const AttnArgs& a, int b, bool& ok) {
   const int kv = a.kv_lens ? a.kv_lens[b] : a.uniform_kv;
   ok = kv >= a.s_q && kv <= a.max_kv;
@@ -188,6 +193,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // slot cur_slot of the chunk (tiles never straddle a page).  Scalar state,
   // advanced by one tile per issue, so no division on the issue path.
   int cur_slot = 0, cur_off = k0 % a.page_size, cur_tile = 0;
+  const int ntiles = (k1 - k0 + TILE - 1) / TILE;
   const uint64_t pool_addr = (uint64_t)(uintptr_t)a.pool;
   const uint32_t page_bytes = (uint32_t)a.page_size * RB;
   const uint32_t num_pages = (uint32_t)min<int64_t>(a.num_pages, 0x7fffffff);
@@ -196,16 +202,20 @@ void attn_bf16_kernel(AttnArgs a) {
     __amdgpu_buffer_rsrc_t r;
     uint32_t dst;
   };
+  // Tiles past the chunk's end are issued too, with an empty resource (their
+  // loads write zeros into a free stage): the tile loop then issues and waits
+  // for a fixed number of loads per pass, with no branches.
   auto prep_tile = [&](int page_id) {  // resource of the cursor's tile, then advance
     // 32-bit scalar arithmetic only: a negative id fails the unsigned compare
     const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_id);
+    const bool real = cur_tile < ntiles;
     const bool pok = page < num_pages;
     // rows of the tile are contiguous within one page; rows past k1 (and a
     // bad page) lie outside the resource and load as zeros
     const int kb = k0 + cur_tile * TILE;
     const uint64_t addr = pool_addr + (uint64_t)(pok ? page : 0u) * page_bytes + (uint32_t)cur_off * RB;
     TileDma d;
-    d.r = make_rsrc((const void*)(uintptr_t)addr, pok ? min(TILE, k1 - kb) * RB : 0);
+    d.r = make_rsrc((const void*)(uintptr_t)addr, (real && pok) ? min(TILE, k1 - kb) * RB : 0);
     d.dst = smem_addr + (cur_tile % NSTAGE) * STAGE + wave * 1024;
     cur_tile += 1;
     cur_off += TILE;
@@ -213,15 +223,16 @@ void attn_bf16_kernel(AttnArgs a) {
       cur_off = 0;
       cur_slot += 1;
     }
-    bad_page |= !pok;
+    bad_page |= real && !pok;
     return d;
   };
+  // page id at the cursor (a stale id past the chunk: its tile is empty)
+  auto cursor_page = [&]() { return split_pages[min(cur_slot, MAX_SPLIT_PAGES - 1)]; };
   auto issue_next = [&](int page_id) {
     const TileDma d = prep_tile(page_id);
 #pragma unroll
     for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(d.r, d.dst + i * 4096, dma_off[i]);
   };
-  const int ntiles = (k1 - k0 + TILE - 1) / TILE;
 
   // ---- tile 0 (vector loads complete in issue order: the queries, then tile 0)
   issue_next(split_pages[0]);
@@ -235,11 +246,10 @@ void attn_bf16_kernel(AttnArgs a) {
   asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
                "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
 #pragma unroll
-  for (int p = 1; p < DEPTH; ++p)
-    if (p < ntiles) issue_next(split_pages[cur_slot]);
+  for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
   // page of the next tile to issue, fetched one tile early to keep the LDS
   // latency off the issue path
-  int next_page = DEPTH < ntiles ? split_pages[cur_slot] : 0;
+  int next_page = cursor_page();
 
   // Accumulator O^T for this wave's 128 latent dims (4 blocks of 32) and all
   // 128 heads of the workgroup (4 blocks of 32): acc[4 * d + hb].
@@ -380,9 +390,7 @@ void attn_bf16_kernel(AttnArgs a) {
     flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
   };
   f32x16 s_nx;  // scores of the next tile
-  if (ntiles > 2) wait_vmcnt<2 * DMA_PER_THREAD>();
-  else if (ntiles > 1) wait_vmcnt<DMA_PER_THREAD>();
-  else wait_vmcnt<0>();
+  wait_vmcnt<2 * DMA_PER_THREAD>();  // tile 0 (tiles 1 and 2, possibly empty, stay in flight)
   __syncthreads();
   {
     const unsigned char* K0 = smem;
@@ -396,22 +404,22 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int j = 0; j < SM_SLOTS; ++j) sm_slot(j, s_nx, k0, true);
     publish();
   }
-  for (int t = 0; t < ntiles; ++t) {
-    const bool has_next = t + 1 < ntiles;
+  // One pass; HAS_NEXT is a compile-time flag so that the interleaved work
+  // carries no branches (the last pass is peeled off).
+  auto pass = [&](const int t, auto has_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     // tile t+1 has landed once at most tile t+2's loads are outstanding; the
     // barrier makes every thread's loads and tile t's P^T visible
-    if (t + 2 < ntiles) wait_vmcnt<DMA_PER_THREAD>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<DMA_PER_THREAD>();
     __syncthreads();
-    // tile t+3 goes to the stage that held tile t-1 (read by the previous
-    // pass); its loads are spread over this pass's PV MFMAs (all waves issuing
-    // at once would queue on the CU's address unit)
-    const bool do_issue = t + DEPTH < ntiles;
-    TileDma nd;
-    if (do_issue) nd = prep_tile(next_page);
+    // tile t+3 (possibly empty) goes to the stage that held tile t-1, read by
+    // the previous pass; its loads are spread over this pass's PV MFMAs (all
+    // waves issuing at once would queue on the CU's address unit)
+    const TileDma nd = prep_tile(next_page);
+    next_page = cursor_page();
     const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
     const int kb_next = k0 + (t + 1) * TILE;
-    if (has_next) {
+    if constexpr (HAS_NEXT) {
       const unsigned char* Kn = smem + ((t + 1) % NSTAGE) * STAGE;
       qk_begin(Kn);
 #pragma unroll
@@ -420,7 +428,6 @@ void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (do_issue && t + DEPTH + 1 < ntiles) next_page = split_pages[cur_slot];
 
     // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head] for this wave's 128
     // dims and all 128 heads: per k step q, 4 dim blocks x 4 head blocks.
@@ -475,18 +482,22 @@ void attn_bf16_kernel(AttnArgs a) {
           if (q == 0 && d == 3) pb[hb] = p_xchg[(hb * 2 + 1) * 64 + lane];
           const int mi = 4 * m + hb;
           // the next tile's softmax, one slot per MFMA
-          if (has_next && mi < SM_SLOTS) sm_slot(mi, s_nx, kb_next, false);
+          if constexpr (HAS_NEXT) {
+            if (mi < SM_SLOTS) sm_slot(mi, s_nx, kb_next, false);
+          }
           // one of tile t+3's loads after every third MFMA
-          if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD && do_issue)
-            dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
+          if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD) dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     // every wave is done with tile t's P^T and rescale slots
     __syncthreads();
-    if (has_next) publish();
-  }
+    if constexpr (HAS_NEXT) publish();
+  };
+  for (int t = 0; t + 1 < ntiles; ++t) pass(t, BoolTag<true>{});
+  pass(ntiles - 1, BoolTag<false>{});
+  wait_vmcnt<0>();  // the empty tiles' loads still write LDS: drain them
   // wait states before VALU reads of accumulators last written by an MFMA
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
