@@ -109,11 +109,12 @@ def run_decode_bench(steps: int, warmup: int):
         step(i, ev.pair(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    attn_list = [ev.elapsed_ms(i) for i in range(steps)]
     ev.close()
     latent_bytes = int(inp.kv_lens.sum()) * cfg.row * 2
     flops = int(inp.kv_lens.sum()) * cfg.n_heads * (cfg.row + cfg.d_c) * 2
-    return dict(inp=inp, wall=wall, attn_ms=attn_ms, latent_bytes=latent_bytes, attn_flops=flops)
+    return dict(inp=inp, wall=wall, attn_ms=float(np.mean(attn_list)), attn_list=attn_list,
+                latent_bytes=latent_bytes, attn_flops=flops)
 
 
 def prefill_flops(s: mi.Shape, L: int) -> dict:
