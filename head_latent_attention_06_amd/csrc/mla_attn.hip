@@ -46,7 +46,9 @@ constexpr int DC = 512, DR = 64, ROW = DC + DR;  // cached row: c^KV then k^R
 constexpr int TILE = 32;                         // keys per LDS tile
 constexpr int RB = ROW * 2;                      // bytes per key row (1152, unpadded)
 constexpr int STAGE = TILE * RB;                 // 36864 bytes per tile
-constexpr int NSTAGE = 4, DEPTH = 3;             // LDS ring, tiles in flight
+// Pass t reads tiles t and t+1 from LDS and issues tile t + DEPTH into the
+// stage that held tile t-1: DEPTH - 1 tiles are in flight behind the two in use.
+constexpr int DEPTH = 3, NSTAGE = DEPTH + 1;
 constexpr int DMA_PER_THREAD = STAGE / 16 / 256; // 9 16-byte loads per thread per tile
 constexpr int WG_HEADS = 128;
 constexpr int MAX_SPLIT_PAGES = 1536;            // page ids of one split, staged in LDS
@@ -390,7 +392,7 @@ void attn_bf16_kernel(AttnArgs a) {
     flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
   };
   f32x16 s_nx;  // scores of the next tile
-  wait_vmcnt<2 * DMA_PER_THREAD>();  // tile 0 (tiles 1 and 2, possibly empty, stay in flight)
+  wait_vmcnt<(DEPTH - 1) * DMA_PER_THREAD>();  // tile 0 (tiles 1 .. DEPTH-1, possibly empty, stay in flight)
   __syncthreads();
   {
     const unsigned char* K0 = smem;
@@ -408,15 +410,19 @@ void attn_bf16_kernel(AttnArgs a) {
   // carries no branches (the last pass is peeled off).
   auto pass = [&](const int t, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    // tile t+1 has landed once at most tile t+2's loads are outstanding; the
-    // barrier makes every thread's loads and tile t's P^T visible
-    wait_vmcnt<DMA_PER_THREAD>();
+    // tile t+1 has landed once at most tiles t+2 .. t+DEPTH-1 are outstanding;
+    // the barrier makes every thread's loads and tile t's P^T visible
+    wait_vmcnt<(DEPTH - 2) * DMA_PER_THREAD>();
     __syncthreads();
     // tile t+3 (possibly empty) goes to the stage that held tile t-1, read by
     // the previous pass; its loads are spread over this pass's PV MFMAs (all
     // waves issuing at once would queue on the CU's address unit)
     const TileDma nd = prep_tile(next_page);
     next_page = cursor_page();
+    // tile t's rescale flags (byte hb for head block hb), read now so the LDS
+    // latency is hidden behind the QK phase
+    uint32_t flags;
+    __builtin_memcpy(&flags, flag_xchg, 4);
     const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
     const int kb_next = k0 + (t + 1) * TILE;
     if constexpr (HAS_NEXT) {
@@ -439,8 +445,6 @@ void attn_bf16_kernel(AttnArgs a) {
       const u32x2 hv = lds_tr16(Kd + pv_off[q][1][d & 1]);
       return u32x4{lo[0], lo[1], hv[0], hv[1]};
     };
-    uint32_t flags;  // byte hb = flag of head block hb, read first, in one LDS access
-    __builtin_memcpy(&flags, flag_xchg, 4);
     u32x4 pb[4];  // P^T fragments of the current k step; step 1 reloads them in place
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) pb[hb] = p_xchg[hb * 2 * 64 + lane];
