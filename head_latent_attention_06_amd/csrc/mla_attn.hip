@@ -149,9 +149,9 @@ void attn_bf16_kernel(AttnArgs a) {
   const int64_t qrow = row;
   const float scale_log2 = a.scale * LOG2E;
 
-  // ---- loads that do not depend on each other, issued back to back: the
-  // chunk's page ids (staged in LDS, keeping block-table reads off the tile
-  // pipeline), then the queries
+  // ---- the chunk's page ids, staged in LDS (keeping block-table reads off
+  // the tile pipeline); waited for before the bulk loads start, so they do
+  // not queue behind them
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int pg_first = k0 / a.page_size;
   const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
@@ -161,20 +161,6 @@ void attn_bf16_kernel(AttnArgs a) {
   for (int k = 0; k < PAGES_PER_THREAD; ++k) {
     const int i = tid + 256 * k, pidx = pg_first + i;
     pid[k] = (i < n_pages && pidx < a.max_pages) ? bt[pidx] : -1;
-  }
-  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
-  // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
-  u32x4 qf[36];
-  {
-    const int nh = wave_on ? min(32, a.H - head0) : 0;
-    const int64_t hrow = qrow * a.H + (wave_on ? head0 : 0);
-    const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
-    const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
-#pragma unroll
-    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
   }
 #pragma unroll
   for (int k = 0; k < PAGES_PER_THREAD; ++k)
@@ -236,9 +222,25 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(d.r, d.dst + i * 4096, dma_off[i]);
   };
 
-  // ---- tile 0 (vector loads complete in issue order: the queries, then tile 0)
+  // ---- tiles 0 .. DEPTH-1 (possibly empty), then the queries: one burst
   issue_next(split_pages[0]);
-  // Wait for the queries (and tile 0) here: left to the compiler, the wait
+#pragma unroll
+  for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
+  // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
+  // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
+  u32x4 qf[36];
+  {
+    const int nh = wave_on ? min(32, a.H - head0) : 0;
+    const int64_t hrow = qrow * a.H + (wave_on ? head0 : 0);
+    const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
+    const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
+#pragma unroll
+    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
+  }
+  // Wait for the queries (and the first tiles) here: left to the compiler, the wait
   // would sit inside the tile loop in front of the MFMAs that read them and
   // would drain the tile loads in flight on every pass.
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
@@ -247,8 +249,6 @@ void attn_bf16_kernel(AttnArgs a) {
                "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]));
   asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
                "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
-#pragma unroll
-  for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
   // page of the next tile to issue, fetched one tile early to keep the LDS
   // latency off the issue path
   int next_page = cursor_page();
@@ -392,7 +392,7 @@ void attn_bf16_kernel(AttnArgs a) {
     flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
   };
   f32x16 s_nx;  // scores of the next tile
-  wait_vmcnt<(DEPTH - 1) * DMA_PER_THREAD>();  // tile 0 (tiles 1 .. DEPTH-1, possibly empty, stay in flight)
+  // (tiles 0 .. DEPTH-1 have landed with the queries)
   __syncthreads();
   {
     const unsigned char* K0 = smem;
