@@ -117,7 +117,8 @@ def run_decode_bench(steps: int, warmup: int):
                 latent_bytes=latent_bytes, attn_flops=flops)
 
 
-def prefill_flops(s: mi.Shape, L: int) -> dict:
+def prefill_flops(s: mi.Shape, L: int, explicit: bool) -> dict:
+    """FLOPs one prefill executes in the given attention form."""
     T = L
     pairs = L * (L + 1) // 2
     H, dh, dr, dc, dcq, d = s.n_heads, s.d_head, s.d_rope, s.d_c, s.d_cq, s.d_model
@@ -126,20 +127,22 @@ def prefill_flops(s: mi.Shape, L: int) -> dict:
         "q_down_proj": 2 * T * dcq * d,
         "q_up_proj": 2 * T * H * dh * dcq,
         "q_rope_proj": 2 * T * H * dr * dcq,
-        "absorb_w_uk": 2 * T * H * dh * dc,
-        "attention": 2 * pairs * H * (dc + dr + dc),
-        "w_uv": 2 * T * H * dc * dh,
     }
+    if explicit:  # k^C, v^C materialised per head; d_qk = 192, d_v = 128
+        f["k_up_proj"] = 2 * T * H * dh * dc
+        f["v_up_proj"] = 2 * T * H * dh * dc
+        f["attention"] = 2 * pairs * H * (dh + dr + dh)
+    else:         # W^UK folded into the query, W^UV after the latent sum
+        f["absorb_w_uk"] = 2 * T * H * dh * dc
+        f["attention"] = 2 * pairs * H * (dc + dr + dc)
+        f["w_uv"] = 2 * T * H * dc * dh
     f["total"] = sum(f.values())
-    # explicit-form attention (k, v materialised per head, d_qk = 192, d_v = 128)
-    f["explicit_equivalent_total"] = f["total"] - f["attention"] - f["absorb_w_uk"] + 2 * pairs * H * (dh + dr + dh) \
-        + 2 * T * H * dh * dc * 2
     return f
 
 
-def run_prefill_bench(steps: int, warmup: int, L: int = 8192):
+def run_prefill_bench(steps: int, warmup: int, form: int, L: int = 8192):
     s = mi.V3
-    cfg = mla.Config()
+    cfg = mla.Config(prefill_form=form)
     w = {k: _up(v) for k, v in mi.weights(3, s).items()}
     h = _up(mi.hidden(3, s, 1, L))
     bt, npages = mi.block_table(3, [L], s.page_size, shuffle=True)
@@ -158,7 +161,9 @@ def run_prefill_bench(steps: int, warmup: int, L: int = 8192):
     wall = time.perf_counter() - t0
     attn_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
     ev.close()
-    return dict(wall=wall, attn_ms=attn_ms, flops=prefill_flops(s, L), L=L)
+    del ws, cache, out
+    torch.cuda.empty_cache()
+    return dict(wall=wall, attn_ms=attn_ms, flops=prefill_flops(s, L, form == mla.PREFILL_EXPLICIT), L=L)
 
 
 def cpu_baseline(inp, min_seconds: float):
@@ -192,20 +197,30 @@ def copy_calibration(n_bytes: int = 1 << 30, reps: int = 5):
 
 
 def run_prefill_summary(args) -> dict:
+    """Both attention forms on the same workload; the explicit form (what
+    mla_prefill picks by itself here) is the main entry, the absorbed form is
+    reported beside it."""
     steps = max(2, args.steps // 4)
-    p = run_prefill_bench(steps, max(1, args.warmup // 2))
-    pms = p["wall"] / steps * 1e3
-    f = p["flops"]
-    achieved = f["attention"] / (p["attn_ms"] * 1e-3) / 1e12
-    return {
-        "workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention",
-        "ms_per_step": round(pms, 3), "tflops_executed": round(f["total"] / (pms * 1e-3) / 1e12, 1),
-        "tokens_per_s": round(p["L"] / (pms * 1e-3), 1),
-        "explicit_equivalent_tflops": round(f["explicit_equivalent_total"] / (pms * 1e-3) / 1e12, 1),
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "kernel_ms": round(p["attn_ms"], 4),
-                     "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4)},
-    }
+    res = {"workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention"}
+    for form, name, kernel in ((mla.PREFILL_EXPLICIT, "explicit", "fa_bf16_kernel"),
+                               (mla.PREFILL_ABSORBED, "absorbed", "attn_bf16_kernel")):
+        p = run_prefill_bench(steps, max(1, args.warmup // 2), form)
+        pms = p["wall"] / steps * 1e3
+        f = p["flops"]
+        achieved = f["attention"] / (p["attn_ms"] * 1e-3) / 1e12
+        r = {
+            "ms_per_step": round(pms, 3), "tflops_executed": round(f["total"] / (pms * 1e-3) / 1e12, 1),
+            "tokens_per_s": round(p["L"] / (pms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "kernel": kernel, "kernel_ms": round(p["attn_ms"], 4),
+                         "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "flops_per_launch": f["attention"]},
+        }
+        if name == "explicit":
+            res.update(r)
+            res["form"] = "explicit"
+        else:
+            res["absorbed_form"] = r
+    return res
 
 
 def measured_traffic(path: str = os.path.join(ROOT, "profiles", "attn_bf16_decode_b64_ctx4096_traffic.md")):

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_RANGE, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
 MLA_F32, MLA_BF16 = 0, 1
+PREFILL_AUTO, PREFILL_ABSORBED, PREFILL_EXPLICIT = 0, 1, 2
+ABI_VERSION = 2  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
 MLA_FLAG_BAD_PAGE, MLA_FLAG_BAD_POS, MLA_FLAG_BAD_LEN, MLA_FLAG_BAD_SEQ = 1, 2, 4, 8
 
 
@@ -32,7 +34,7 @@ class _Config(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("prefill_form", ctypes.c_int32)]
 
 
 class _Cache(ctypes.Structure):
@@ -102,6 +104,7 @@ class Config:
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     dtype: torch.dtype = torch.bfloat16
+    prefill_form: int = PREFILL_AUTO  # PREFILL_AUTO / PREFILL_ABSORBED / PREFILL_EXPLICIT
 
     @property
     def row(self) -> int:
@@ -111,7 +114,7 @@ class Config:
         scale = self.softmax_scale if self.softmax_scale is not None else (self.d_head + self.d_rope) ** -0.5
         dt = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32}[self.dtype]
         return _Config(self.n_heads, self.d_head, self.d_rope, self.d_c, self.d_cq, self.d_model, self.page_size,
-                       scale, self.rope_base, self.rms_eps, dt)
+                       scale, self.rope_base, self.rms_eps, dt, self.prefill_form)
 
 
 @dataclass

@@ -36,6 +36,7 @@ mla_status check_cfg(const mla_config* c, bool* bf16) {
       c->page_size <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!(c->softmax_scale > 0.f) || !(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return MLA_ERR_INVALID_ARG;
+  if (c->prefill_form < MLA_PREFILL_AUTO || c->prefill_form > MLA_PREFILL_EXPLICIT) return MLA_ERR_INVALID_ARG;
   if (c->page_size % 32 != 0 || (c->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
   if (c->dtype == MLA_BF16) {
     *bf16 = true;
@@ -104,18 +105,44 @@ DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, i
   return d;
 }
 
+// The explicit prefill form: bf16 with the head widths its kernel is built for.
+bool explicit_supported(const mla_config* c, bool bf16) { return bf16 && c->d_head == 128 && c->d_rope == 64; }
+
+// Form of the prefill attention.  FLOPs per head beyond the shared projections
+// (S cached rows, L new ones, pairs = L S + L (L + 1) / 2):
+//   explicit  2 * 2 * d_c * d_h * (S + L)  +  2 (d_h + d_h^R + d_h) pairs
+//   absorbed  2 * 2 * d_c * d_h * L        +  2 (d_c + d_h^R + d_c) pairs
+// so with V3 widths the explicit form is cheaper once 768 L (2 S + L) >= 262144 S.
+mla_status prefill_form(const mla_config* c, bool bf16, int32_t L, int32_t start_pos, bool* use_explicit) {
+  const bool ok = explicit_supported(c, bf16);
+  if (c->prefill_form == MLA_PREFILL_EXPLICIT) {
+    if (!ok) return MLA_ERR_UNSUPPORTED;
+    *use_explicit = true;
+  } else if (c->prefill_form == MLA_PREFILL_ABSORBED) {
+    *use_explicit = false;
+  } else {
+    // explicit - absorbed = 4 d_c d_h S - 4 (d_c - d_h) pairs
+    const int64_t S = start_pos;
+    const int64_t pairs = (int64_t)L * S + (int64_t)L * (L + 1) / 2;
+    *use_explicit = ok && (int64_t)c->d_c * c->d_head * S <= (int64_t)(c->d_c - c->d_head) * pairs;
+  }
+  return MLA_OK;
+}
+
 struct PrefillWs {
   float *kv_raw, *cq_raw, *qr_raw, *rope_cs, *part_ml;
   void *cq, *qc, *q_abs, *o_lat, *part_o;
+  void *qr, *kvg, *kc, *vc;  // explicit form
   int32_t* plan;
   int64_t max_items;
-  bool split;
+  bool split, use_explicit;
 };
 
-PrefillWs prefill_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, int32_t start_pos, void* ws,
-                         size_t* total) {
+PrefillWs prefill_layout(const mla_config* c, bool bf16, bool use_explicit, int32_t B, int32_t L, int32_t start_pos,
+                         void* ws, size_t* total) {
   Carve cv(ws);
   PrefillWs p{};
+  p.use_explicit = use_explicit;
   const int64_t T = (int64_t)B * L, H = c->n_heads, row = c->d_c + c->d_rope;
   const size_t e = bf16 ? 2 : 4;
   p.rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
@@ -124,6 +151,15 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, i
   p.cq = cv.take(T * c->d_cq * e);
   p.qc = cv.take(T * H * c->d_head * e);
   p.qr_raw = (float*)cv.take(T * H * c->d_rope * 4);
+  if (use_explicit) {
+    const int64_t nk = (int64_t)B * (start_pos + L);
+    p.qr = cv.take(T * H * c->d_rope * e);
+    p.kvg = cv.take(nk * row * e);
+    p.kc = cv.take(nk * H * c->d_head * e);
+    p.vc = cv.take(nk * H * c->d_head * e);
+    *total = cv.off;
+    return p;
+  }
   p.q_abs = cv.take(T * H * row * e);
   p.o_lat = cv.take(T * H * c->d_c * e);
   if (bf16) {
@@ -253,6 +289,43 @@ mla_status attend(const mla_config* c, bool bf16, AttnArgs a, int32_t* plan, int
   return launch_gemm(bf16, g, st);
 }
 
+// Steps (3) to (10) of the explicit form, after q^C and the raw q^R are in the
+// workspace: RoPE of q^R, k^C = W^UK c and v^C = W^UV c for rows
+// [0, start_pos + L) of every sequence, then causal attention.
+mla_status prefill_explicit(const mla_config* c, const mla_kv_cache* k, const mla_weights* w, int32_t B, int32_t L,
+                            int32_t start_pos, const PrefillWs& p, void* out, hipStream_t st, void* ev0, void* ev1) {
+  const int T = B * L, H = c->n_heads, row = c->d_c + c->d_rope, kv_end = start_pos + L;
+  const int nk = B * kv_end;
+  MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.qr, c->d_rope, 0, T, H, c->d_rope, 1, st));
+  GatherArgs g{};
+  g.pool = k->pool; g.num_pages = k->num_pages;
+  g.block_table = k->block_table; g.max_pages = k->max_pages_per_seq; g.page_size = c->page_size;
+  g.B = B; g.kv_end = kv_end; g.row = row;
+  g.err_flags = k->err_flags;
+  g.out = p.kvg;
+  MLA_HIP(launch_gather_rows(g, st));
+  // k^C[j, i, :] = W_i^UK c_j and v^C[j, i, :] = W_i^UV c_j: [nk, d_c] x [H d_h, d_c]^T
+  mla_status s;
+  if ((s = launch_gemm(true, gemm(p.kvg, row, 0, w->w_uk, c->d_c, 0, p.kc, (int64_t)H * c->d_head, 0, nk,
+                                  H * c->d_head, c->d_c, 1, false, true), st)) != MLA_OK)
+    return s;
+  if ((s = launch_gemm(true, gemm(p.kvg, row, 0, w->w_uv, c->d_c, 0, p.vc, (int64_t)H * c->d_head, 0, nk,
+                                  H * c->d_head, c->d_c, 1, false, true), st)) != MLA_OK)
+    return s;
+  FaArgs a{};
+  a.qc = p.qc; a.qr = p.qr;
+  a.kc = p.kc; a.vc = p.vc;
+  a.kr = (const unsigned char*)p.kvg + (size_t)c->d_c * 2;
+  a.ld_kr = row;
+  a.B = B; a.L = L; a.H = H; a.start_pos = start_pos; a.kv_end = kv_end;
+  a.scale = c->softmax_scale;
+  a.out = out;
+  if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
+  MLA_HIP(launch_fa_bf16(a, st));
+  if (ev1) MLA_HIP(hipEventRecord((hipEvent_t)ev1, st));
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,7 +404,9 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t 
   mla_status s = check_cfg(cfg, &bf16);
   if (s != MLA_OK) return s;
   if (!bytes || B < 0 || L < 0 || start_pos < 0) return MLA_ERR_INVALID_ARG;
-  prefill_layout(cfg, bf16, B, L, start_pos, nullptr, bytes);
+  bool use_explicit;
+  if ((s = prefill_form(cfg, bf16, L, start_pos, &use_explicit)) != MLA_OK) return s;
+  prefill_layout(cfg, bf16, use_explicit, B, L, start_pos, nullptr, bytes);
   return MLA_OK;
 }
 
@@ -358,8 +433,11 @@ mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache
   const int64_t kv_end = (int64_t)start_pos + L;
   if (kv_end > (int64_t)cache->max_pages_per_seq * cfg->page_size || kv_end > (1 << 30)) return MLA_ERR_OUT_OF_RANGE;
   if ((int64_t)B * L > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  bool use_explicit;
+  if ((s = prefill_form(cfg, bf16, L, start_pos, &use_explicit)) != MLA_OK) return s;
+  if (use_explicit && (int64_t)B * kv_end > (1 << 24)) return MLA_ERR_UNSUPPORTED;
   size_t need;
-  PrefillWs p = prefill_layout(cfg, bf16, B, L, start_pos, ws, &need);
+  PrefillWs p = prefill_layout(cfg, bf16, use_explicit, B, L, start_pos, ws, &need);
   if (need > ws_bytes) return MLA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int T = B * L, H = cfg->n_heads, row = cfg->d_c + cfg->d_rope;
@@ -378,6 +456,7 @@ mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache
   if ((s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_qr, cfg->d_cq, 0, p.qr_raw, (int64_t)H * cfg->d_rope, 0,
                                   T, H * cfg->d_rope, cfg->d_cq, 1, false, false), st)) != MLA_OK)
     return s;
+  if (p.use_explicit) return prefill_explicit(cfg, cache, w, B, L, start_pos, p, out, st, attn_start, attn_stop);
   MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.q_abs, row, cfg->d_c, T, H, cfg->d_rope, bf16, st));
   // absorption: q_lat_i = W_i^UK^T q^C_i  (batched over heads, W_i^UK given [d_h, d_c])
   if ((s = launch_gemm(bf16, gemm(p.qc, (int64_t)H * cfg->d_head, cfg->d_head, w->w_uk, cfg->d_c,

@@ -104,4 +104,32 @@ hipError_t launch_rope_heads(const float* x, const float* cs, int32_t table_rows
                              int64_t ld_out, int32_t out_off, int32_t T, int32_t H, int32_t d_rope,
                              int32_t bf16_out, hipStream_t st);
 
+// Explicit-form causal prefill attention (d_qk = 128 + 64, d_v = 128, bf16).
+// Query row t of sequence b sits at position start_pos + t and sees keys
+// [0, start_pos + t] of that sequence.  Keys: row (b * kv_end + j) of kc / vc
+// [*, H, 128] and of kr (first 64 of each row, row stride ld_kr elements).
+struct FaArgs {
+  const void* qc;             // [B * L, H, 128] q^C
+  const void* qr;             // [B * L, H, 64] q^R (rotated)
+  const void* kc;             // [B * kv_end, H, 128] k^C = W^UK c
+  const void* vc;             // [B * kv_end, H, 128] v^C = W^UV c
+  const void* kr;             // [B * kv_end, ld_kr]: first 64 = k^R (rotated)
+  int32_t ld_kr;
+  int32_t B, L, H, start_pos, kv_end;
+  float scale;
+  void* out;                  // [B * L, H, 128]
+};
+hipError_t launch_fa_bf16(const FaArgs& a, hipStream_t st);
+
+// Rows [0, kv_end) of each sequence's paged cache, copied to
+// out [B * kv_end, row] (bf16).  Missing pages give zero rows and set err_flags.
+struct GatherArgs {
+  const void* pool; int64_t num_pages;
+  const int32_t* block_table; int32_t max_pages, page_size;
+  int32_t B, kv_end, row;
+  int32_t* err_flags;
+  void* out;
+};
+hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t st);
+
 }  // namespace mla

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,
@@ -59,6 +59,18 @@ typedef enum {
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Which algebraically equal form mla_prefill computes attention in.
+ *  ABSORBED: W_i^UK folded into the query, W_i^UV applied after the weighted
+ *            sum of latents (the 【思考】 passage on absorption); scores are
+ *            576-wide dot products with the cached rows.
+ *  EXPLICIT: k^C = W^UK c and v^C = W^UV c materialised per head for the
+ *            sequence's rows (section 2), then causal attention with 192-wide
+ *            keys and 128-wide values (the ten-step list as written).  bf16
+ *            with d_head = 128 and d_rope = 64 only.
+ *  AUTO:     EXPLICIT where supported and it takes fewer FLOPs (long new
+ *            chunks), else ABSORBED. */
+typedef enum { MLA_PREFILL_AUTO = 0, MLA_PREFILL_ABSORBED = 1, MLA_PREFILL_EXPLICIT = 2 } mla_prefill_form;
 
 /* Layer dimensions (host struct).  Names follow the notes page's symbols. */
 typedef struct {
@@ -73,6 +85,7 @@ typedef struct {
   float rope_base;     /* theta_p = rope_base^(-2p/d_rope)                 */
   float rms_eps;       /* RMSNorm epsilon                                  */
   int32_t dtype;       /* mla_dtype                                        */
+  int32_t prefill_form; /* mla_prefill_form (mla_prefill only)             */
 } mla_config;
 
 /* Paged latent cache (host struct holding device pointers).
@@ -143,7 +156,12 @@ mla_status mla_project_kv(const mla_config* cfg, const mla_kv_cache* cache, cons
  *   o[b, t, i, :] = W_i^UV sum_{j <= start_pos+t} a_j c_j   (d_head values)
  * over all cached rows of sequence b (rows [0, start_pos) must already be
  * present).  h [B, L, d_model]; out [B, L, n_heads, d_head]; both cfg->dtype.
- * The output stops at o (W^O is not applied). */
+ * The output stops at o (W^O is not applied).  cfg->prefill_form picks the
+ * form of the attention (see mla_prefill_form); both give the same o up to
+ * rounding.  MLA_PREFILL_EXPLICIT on a shape it does not serve returns
+ * MLA_ERR_UNSUPPORTED.  The explicit form's workspace holds k^C and v^C of
+ * rows [0, start_pos + L) of every sequence: B * (start_pos + L) * n_heads *
+ * d_head * 4 bytes. */
 mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t L, int32_t start_pos,
                                       size_t* bytes);
 mla_status mla_prefill(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import head_latent_attention_06_amd as mla
 
@@ -34,7 +35,9 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == mla.ABI_VERSION
+    hdr = open(HEADER).read()
+    assert f"#define MLA_ABI_VERSION {mla.ABI_VERSION}" in hdr
     for s in range(6):
         assert mla.status_string(s).startswith("MLA_")
     assert "unknown" in mla.status_string(99)
@@ -104,3 +107,27 @@ def test_prefill_and_append_argument_errors(lib):
     assert lib.mla_cache_append(c, k, None, FAKE, FAKE, FAKE, FAKE, 5, 1, None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_cache_append(c, k, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_project_kv(c, k, ctypes.byref(w), FAKE, 1, 10, 0, FAKE, 16, None) == mla.MLA_ERR_WORKSPACE
+
+
+def _prefill_ws(lib, B, L, start, **kw):
+    n = ctypes.c_size_t()
+    st = lib.mla_prefill_workspace_size(ctypes.byref(_cfg(**kw)), B, L, start, ctypes.byref(n))
+    return st, n.value
+
+
+def test_prefill_form_selection(lib):
+    """The explicit form's workspace holds k^C and v^C of every visible row;
+    AUTO takes it for long new chunks and the absorbed form for short chunks
+    after a long cached prefix."""
+    st_e, ws_e = _prefill_ws(lib, 1, 8192, 0, prefill_form=mla.PREFILL_EXPLICIT)
+    st_a, ws_a = _prefill_ws(lib, 1, 8192, 0, prefill_form=mla.PREFILL_ABSORBED)
+    assert st_e == mla.MLA_OK and st_a == mla.MLA_OK
+    assert ws_e >= 2 * 8192 * 128 * 128 * 2
+    assert _prefill_ws(lib, 1, 8192, 0)[1] == ws_e
+    # 16 new tokens after 8192 cached ones: absorbed is fewer FLOPs
+    assert _prefill_ws(lib, 1, 16, 8192)[1] == _prefill_ws(lib, 1, 16, 8192, prefill_form=mla.PREFILL_ABSORBED)[1]
+    # fp32 has no explicit kernel: AUTO falls back, EXPLICIT is refused
+    kw = dict(dtype=torch.float32, n_heads=4, d_head=16, d_rope=8, d_c=32, d_cq=48, d_model=64)
+    assert _prefill_ws(lib, 1, 64, 0, **kw)[0] == mla.MLA_OK
+    assert _prefill_ws(lib, 1, 64, 0, prefill_form=mla.PREFILL_EXPLICIT, **kw)[0] == mla.MLA_ERR_UNSUPPORTED
+    assert _prefill_ws(lib, 1, 64, 0, prefill_form=7)[0] == mla.MLA_ERR_INVALID_ARG

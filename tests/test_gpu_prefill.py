@@ -1,5 +1,6 @@
 """Prefill parity (all ten steps: projections, RMSNorm, RoPE, cache append,
-causal absorbed attention, W^UV) against the float64 explicit oracle."""
+causal attention in the absorbed form and in the explicit form) against the
+float64 explicit oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +15,14 @@ pytestmark = pytest.mark.gpu
 WNAMES = ("w_dq", "g_q", "w_uq", "w_qr", "w_dkv", "g_kv", "w_kr", "w_uk", "w_uv")
 
 
+FORMS = [pytest.param(mla.PREFILL_ABSORBED, id="absorbed"), pytest.param(mla.PREFILL_EXPLICIT, id="explicit")]
+
+
 def _prefill(shape, dtype, config_id, B, L, start_pos=0, gain_spread=0.0, shuffle=True, cache=None, w=None,
-             h=None):
+             h=None, form=mla.PREFILL_AUTO):
     bf16 = dtype == torch.bfloat16
     cfg = config(shape, dtype)
+    cfg.prefill_form = form
     if w is None:
         w = mi.weights(config_id, shape, bf16=bf16, gain_spread=gain_spread)
     if h is None:
@@ -75,10 +80,13 @@ def test_prefill_chunked_matches_whole_fp32():
     assert rel_l2(host(out_tail)[0], ref) <= F32_TOL
 
 
-def test_prefill_v3_small_bf16_full():
-    """DeepSeek-V3 shapes, B=2, L=96 (several 32-key tiles and a ragged tail)."""
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("L", [96, 300])
+def test_prefill_v3_small_bf16_full(form, L):
+    """DeepSeek-V3 shapes, B=2: L=96 spans several 32-key tiles with a ragged
+    tail; L=300 spans two 256-query groups and five 64-key tiles."""
     s = mi.V3
-    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 31, 2, 96)
+    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 31, 2, L, form=form)
     got = host(out)
     assert np.isfinite(got).all()
     for b in range(2):
@@ -86,16 +94,17 @@ def test_prefill_v3_small_bf16_full():
         err = rel_l2(got[b], ref)
         print(f"b={b} rel_l2={err:.3e}")
         assert err <= BF16_TOL
-        gathered = om.paged_gather(host(cache.pool), cache.block_table.cpu().numpy(), b, 96, s.page_size)
+        gathered = om.paged_gather(host(cache.pool), cache.block_table.cpu().numpy(), b, L, s.page_size)
         assert rel_l2(gathered, rows) <= BF16_TOL
     assert int(cache.err_flags.item()) == 0
 
 
-def test_prefill_v3_8192_sampled():
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_v3_8192_sampled(form):
     """B=1, L=8192 causal prefill at DeepSeek-V3 shapes; oracle on sampled (token, head)."""
     s = mi.V3
     L = 8192
-    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 3, 1, L)
+    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 3, 1, L, form=form)
     got = host(out)[0]
     assert np.isfinite(got).all()
     tokens = np.array([0, 1, 31, 32, 1000, 4095, 4096, 8190, 8191])
@@ -109,16 +118,18 @@ def test_prefill_v3_8192_sampled():
     assert int(cache.err_flags.item()) == 0
 
 
-def test_prefill_bf16_chunked_matches_whole():
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_bf16_chunked_matches_whole(form):
     """V3 shapes: prefill of 160 tokens == 96 tokens, then 64 more at start_pos=96."""
     s = mi.V3
     w = mi.weights(32, s)
     h = mi.hidden(32, s, 1, 160)
-    cfg, cache, _, _, out_all = _prefill(s, torch.bfloat16, 32, 1, 160, w=w, h=h)
+    cfg, cache, _, _, out_all = _prefill(s, torch.bfloat16, 32, 1, 160, w=w, h=h, form=form)
     bt, npages = mi.block_table(33, [160], s.page_size, shuffle=True)
     cache2 = paged_cache(cfg, npages, bt)
-    _prefill(s, torch.bfloat16, 32, 1, 96, w=w, h=h[:, :96], cache=cache2)
-    _, _, _, _, out_tail = _prefill(s, torch.bfloat16, 32, 1, 64, start_pos=96, w=w, h=h[:, 96:], cache=cache2)
+    _prefill(s, torch.bfloat16, 32, 1, 96, w=w, h=h[:, :96], cache=cache2, form=form)
+    _, _, _, _, out_tail = _prefill(s, torch.bfloat16, 32, 1, 64, start_pos=96, w=w, h=h[:, 96:], cache=cache2,
+                                    form=form)
     ref, _ = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=np.arange(96, 160))
     assert rel_l2(host(out_tail)[0], ref) <= BF16_TOL
     assert rel_l2(host(out_tail)[0], host(out_all)[0, 96:]) <= 5e-3
