@@ -22,6 +22,8 @@
 // domain with the lazy rescale of the latent kernel.
 #include <math.h>
 
+#include <utility>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -31,13 +33,33 @@ namespace {
 constexpr int FA_DH = 128, FA_DR = 64;        // d_h (q^C, k^C, v^C) and d_h^R
 constexpr int FA_KT = 64;                     // keys per tile
 constexpr int FA_QW = 64, FA_QG = 4 * FA_QW;  // queries per wave / per workgroup
-// one LDS stage: k^C rows (256 B), k^R rows (128 B), v^C rows (256 B) of 64 keys
-constexpr int FA_KC = 0, FA_KR = FA_KT * 256, FA_V = FA_KR + FA_KT * 128;
-constexpr int FA_STAGE = FA_V + FA_KT * 256;  // 40960 bytes
-constexpr int FA_NSTAGE = 3;                  // tile t in use, t+1 and t+2 in flight
+// LDS: a ring of FA_NK key stages (k^C rows of 256 B, then k^R rows of
+// 128 B, 64 keys) and a ring of FA_NV value stages (v^C rows of 256 B).  While
+// tile t's softmax runs, tile t+1's keys and tile t-1's values are read and
+// tiles t+2, t+3 are in flight, so key rows live 3 tile steps and value rows 5.
+constexpr int FA_KR = FA_KT * 256, FA_KSTAGE = FA_KR + FA_KT * 128;  // 24576
+constexpr int FA_VSTAGE = FA_KT * 256;                               // 16384
+constexpr int FA_NK = 3, FA_NV = 5;
+constexpr int FA_VBASE = FA_NK * FA_KSTAGE;
+constexpr int FA_LDS = FA_VBASE + FA_NV * FA_VSTAGE;  // 155648 bytes
 constexpr int FA_DMA = 10;                    // 16-byte loads per thread per tile
 constexpr float FA_LOG2E = 1.4426950408889634f;
 constexpr float FA_SLACK = 8.0f;
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}),
+// each a separate instantiation, so every index is a compile-time constant
+template <typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const void* base, int32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -58,11 +80,14 @@ template <int N>
 __device__ __forceinline__ void fa_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+// LDS reads at a byte address within the workgroup's LDS
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short fa_s16x4;
-__device__ __forceinline__ u32x2 fa_tr16(const unsigned char* p) {
-  const fa_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) fa_s16x4*)(__attribute__((address_space(3))) unsigned char*)p);
+__device__ __forceinline__ u32x2 fa_tr16(uint32_t addr) {
+  const fa_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) fa_s16x4*)addr);
   return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x4 fa_lds16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)addr;
 }
 template <typename T>
 __device__ __forceinline__ const T* fa_uniform(const T* p) {
@@ -70,6 +95,46 @@ __device__ __forceinline__ const T* fa_uniform(const T* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// Causal mask of one 32x32 S^T tuple in place: register i of the lane holds
+// key row 8 (i/4) + i%4 (plus the lane's offset folded into thr); rows past
+// thr become -inf.  In asm so the tuple keeps its registers.
+__device__ __forceinline__ void fa_causal_mask(f32x16& s, int thr) {
+#define FA_MASK1(i, c) "v_cmp_gt_i32 vcc, " #c ", %16\n\tv_cndmask_b32 %" #i ", %" #i ", %17, vcc\n\t"
+  asm volatile(FA_MASK1(0, 0) FA_MASK1(1, 1) FA_MASK1(2, 2) FA_MASK1(3, 3) FA_MASK1(4, 8) FA_MASK1(5, 9)
+               FA_MASK1(6, 10) FA_MASK1(7, 11) FA_MASK1(8, 16) FA_MASK1(9, 17) FA_MASK1(10, 18) FA_MASK1(11, 19)
+               FA_MASK1(12, 24) FA_MASK1(13, 25) FA_MASK1(14, 26) FA_MASK1(15, 27)
+               : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]), "+v"(s[4]), "+v"(s[5]), "+v"(s[6]), "+v"(s[7]),
+                 "+v"(s[8]), "+v"(s[9]), "+v"(s[10]), "+v"(s[11]), "+v"(s[12]), "+v"(s[13]), "+v"(s[14]),
+                 "+v"(s[15])
+               : "v"(thr), "v"(-INFINITY)
+               : "vcc");
+#undef FA_MASK1
+}
+// The MFMA order of a tile step: per key step of the value product, units
+// "QPQPQPQPQOQ" (Q: a score fragment, P: value block d = 0..3, O: row sum),
+// 44 units in all (24 Q, 16 P, 4 O).
+constexpr char fa_unit_kind(int u) { return "QPQPQPQPQOQ"[u % 11]; }
+constexpr int fa_unit_q(int u) {  // score fragment of unit u (0..23)
+  int n = 0;
+  for (int v = 0; v < u; ++v) n += fa_unit_kind(v) == 'Q';
+  return n;
+}
+constexpr int fa_unit_load(int u) {  // position of unit u's fragment in load order (0..39)
+  int n = 0;
+  for (int v = 0; v < u; ++v) n += fa_unit_kind(v) != 'O';
+  return n;
+}
+constexpr int fa_load_unit(int g) {  // unit whose fragment is load g
+  for (int u = 0; u < 44; ++u)
+    if (fa_unit_kind(u) != 'O' && fa_unit_load(u) == g) return u;
+  return -1;
+}
+// max of three floats (v_max3_f32; the inputs are never signalling NaNs)
+__device__ __forceinline__ float fa_max3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
 }
 // multiply the 16 AGPRs of one accumulator tuple by a per-lane factor
 __device__ __forceinline__ void fa_scale_tuple(f32x16& t, float alpha) {
@@ -87,7 +152,7 @@ __device__ __forceinline__ void fa_scale_tuple(f32x16& t, float alpha) {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bf16_kernel(FaArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[FA_NSTAGE * FA_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[FA_LDS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -110,38 +175,59 @@ void fa_bf16_kernel(FaArgs a) {
   //   k^C: c ^ (r & 15)        k^R: c ^ ((r >> 1) & 7)        v^C: c ^ 4 (r & 3)
   // make the QK fragment reads and the transposing V reads conflict-free.
   const int64_t krow_bytes = (int64_t)H * FA_DH * 2;
-  int32_t dma_off[FA_DMA];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {  // k^C and v^C: instructions 4i + wave of 16
-    const int P = (4 * i + wave) * 64 + lane, r = P >> 4, s = P & 15;
-    dma_off[i] = (int32_t)(r * krow_bytes + ((s ^ (r & 15)) * 16));
-    dma_off[6 + i] = (int32_t)(r * krow_bytes + ((s ^ (4 * (r & 3))) * 16));
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {  // k^R: instructions 4i + wave of 8
-    const int P = (4 * i + wave) * 64 + lane, r = P >> 3, s = P & 7;
-    dma_off[4 + i] = r * (a.ld_kr * 2) + ((s ^ ((r >> 1) & 7)) * 16);
-  }
+  // Instruction i of wave w moves rows 4 (4i + w) .. +3 (k^C, v^C: 16 chunks
+  // per row) or 8 (4i + w) .. +7 (k^R: 8 chunks); the swizzle of those rows
+  // depends on the lane only, so one per-lane offset per source serves every
+  // instruction and the row group is folded into the buffer resource.
+  const int ldkr2 = a.ld_kr * 2;
+  const int32_t dkc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * wave + (lane >> 4)));
+  const int32_t dvc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
+  const int32_t dkr = (lane >> 3) * ldkr2 + 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
   const int64_t key_base = (int64_t)b * a.kv_end;
-  auto issue_tile = [&](int t) {  // tile t (possibly past the end: empty resources)
+  // Sources of tile t (possibly past the end: empty resources) and its ten
+  // 16-byte-per-lane loads: n < 8 k^C / v^C rows 4 (4 (n/2) + w) .., n >= 8
+  // k^R rows 8 (4 (n-8) + w) ..
+  struct TileSrc {
+    const unsigned char *kc, *vc, *kr;
+    int32_t nb_kv, nb_r;
+    uint32_t ks, vs;
+  };
+  auto tile_src = [&](int t) {
     const int kb0 = t * FA_KT;
     const int rows = max(0, min(FA_KT, kv_hi - kb0));
-    const bf16* kc = fa_uniform((const bf16*)a.kc + (key_base + kb0) * H * FA_DH + head * FA_DH);
-    const bf16* vc = fa_uniform((const bf16*)a.vc + (key_base + kb0) * H * FA_DH + head * FA_DH);
-    const bf16* kr = fa_uniform((const bf16*)a.kr + (key_base + kb0) * a.ld_kr);
-    const int32_t nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
-    const int32_t nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * a.ld_kr * 2 + FA_DR * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rkc = fa_rsrc(kc, nb_kv), rvc = fa_rsrc(vc, nb_kv), rkr = fa_rsrc(kr, nb_r);
-    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_addr + (t % FA_NSTAGE) * FA_STAGE);
+    TileSrc ts;
+    ts.kc = fa_uniform((const unsigned char*)a.kc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2);
+    ts.vc = fa_uniform((const unsigned char*)a.vc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2);
+    ts.kr = fa_uniform((const unsigned char*)a.kr + (key_base + kb0) * ldkr2);
+    ts.nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
+    ts.nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
+    ts.ks = __builtin_amdgcn_readfirstlane(smem_addr + (t % FA_NK) * FA_KSTAGE);
+    ts.vs = __builtin_amdgcn_readfirstlane(smem_addr + FA_VBASE + (t % FA_NV) * FA_VSTAGE);
+    return ts;
+  };
+  auto dma_one = [&](const TileSrc& ts, int n) {
+    if (n < 8) {
+      const int i = n >> 1;
+      const int32_t u = __builtin_amdgcn_readfirstlane((int32_t)(4 * (4 * i + wave) * krow_bytes));
+      const int32_t nb = max(0, ts.nb_kv - u);
+      if (n & 1)
+        fa_dma16(fa_rsrc(fa_uniform(ts.vc + u), nb), ts.vs + (4 * i + wave) * 1024, dvc);
+      else
+        fa_dma16(fa_rsrc(fa_uniform(ts.kc + u), nb), ts.ks + (4 * i + wave) * 1024, dkc);
+    } else {
+      const int i = n - 8;
+      const int32_t u = __builtin_amdgcn_readfirstlane(8 * (4 * i + wave) * ldkr2);
+      fa_dma16(fa_rsrc(fa_uniform(ts.kr + u), max(0, ts.nb_r - u)), ts.ks + FA_KR + (4 * i + wave) * 1024, dkr);
+    }
+  };
+  auto issue_tile = [&](int t) {
+    const TileSrc ts = tile_src(t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa_dma16(rkc, st + FA_KC + (4 * i + wave) * 1024, dma_off[i]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) fa_dma16(rkr, st + FA_KR + (4 * i + wave) * 1024, dma_off[4 + i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa_dma16(rvc, st + FA_V + (4 * i + wave) * 1024, dma_off[6 + i]);
+    for (int n = 0; n < FA_DMA; ++n) dma_one(ts, n);
   };
   issue_tile(0);
   issue_tile(1);
+  issue_tile(2);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T): query block qb (32 queries),
   // k step s covers dims 16s .. 16s+15 (s < 8: q^C, s >= 8: q^R).  Queries past
@@ -165,26 +251,17 @@ void fa_bf16_kernel(FaArgs a) {
       for (int s = 0; s < 4; ++s) qf[qb][8 + s] = fa_ld16(rr, l32 * H * FA_DR * 2 + 32 * s + 16 * hi);
     }
   }
-  // the queries (and tile 0) are waited for here, not inside the tile loop
-  asm volatile("" ::"v"(qf[0][0]), "v"(qf[0][1]), "v"(qf[0][2]), "v"(qf[0][3]), "v"(qf[0][4]), "v"(qf[0][5]),
-               "v"(qf[0][6]), "v"(qf[0][7]), "v"(qf[0][8]), "v"(qf[0][9]), "v"(qf[0][10]), "v"(qf[0][11]));
-  asm volatile("" ::"v"(qf[1][0]), "v"(qf[1][1]), "v"(qf[1][2]), "v"(qf[1][3]), "v"(qf[1][4]), "v"(qf[1][5]),
-               "v"(qf[1][6]), "v"(qf[1][7]), "v"(qf[1][8]), "v"(qf[1][9]), "v"(qf[1][10]), "v"(qf[1][11]));
 
-  // per-lane LDS offsets.  QK A operand (key row 32 kb + l32, chunk 2s + hi):
-  int kc_off[8], kr_off[4];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kc_off[s] = FA_KC + l32 * 256 + (((2 * s + hi) ^ (l32 & 15)) * 16);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) kr_off[s] = FA_KR + l32 * 128 + (((2 * s + hi) ^ ((l32 >> 1) & 7)) * 16);
-  // V^T A operand via transposing reads: for key step ks (16 keys), read r
-  // (keys 16 ks + 8 r + 4 hi + jl/4), dim block d: chunk 4 d + 2 g1 + (jl&3)/2
-  // of the row, half jl & 1.
+  // Per-lane LDS read addresses.  QK A operand: key row 32 kb + l32, chunk
+  // 2s + hi (k^C) or 2s' + hi (k^R); V^T A operand via transposing reads: key
+  // step ks, read r: row 16 ks + 8 r + 4 hi + jl/4, dim block d: chunk
+  // 4 d + 2 g1 + (jl&3)/2, half jl & 1.  With the swizzles above, the address
+  // of fragment s (or d) is a per-lane base XOR 32 s (64 d): the stage bases
+  // and the smem base have no bits where s and d land.
   const int g1 = (lane >> 4) & 1, jl = lane & 15, rl = 4 * hi + (jl >> 2);
-  int v_off[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    v_off[d] = FA_V + rl * 256 + ((4 * (d ^ (rl & 3)) + 2 * g1 + ((jl & 3) >> 1)) * 16) + 8 * (jl & 1);
+  const uint32_t kx = l32 * 256 + 16 * (hi ^ (l32 & 1)) + 32 * ((l32 & 15) >> 1);
+  const uint32_t rx = FA_KR + l32 * 128 + 16 * (hi ^ ((l32 >> 1) & 1)) + 32 * (((l32 >> 1) & 7) >> 1);
+  const uint32_t vx = rl * 256 + 64 * (rl & 3) + 32 * g1 + 16 * ((jl & 3) >> 1) + 8 * (jl & 1);
 
   f32x16 acc[4][2];  // O^T [dim block][query block], AGPRs
 #pragma unroll
@@ -193,113 +270,242 @@ void fa_bf16_kernel(FaArgs a) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[d][qb][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // row sums of P: ones x P^T on the MFMA, every register of a lane holds its
+  // query's sum (of the same bf16 P values as the numerator)
+  f32x16 acc_l[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_l[qb][i] = 0.f;
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+  float m_run[2] = {-INFINITY, -INFINITY};
   const int qpos0 = a.start_pos + q0 + FA_QW * wave;  // position of the wave's first query
-
   // tiles whose keys are all after every query of this wave are only moved, not used
   const int nt_wave = min(ntiles, (qpos0 + FA_QW - 1) / FA_KT + 1);
-  int t = 0;
-  for (; t < nt_wave; ++t) {
-    // tile t has landed once at most tile t+1's loads are outstanding
-    fa_wait_vmcnt<FA_DMA>();
-    __syncthreads();
-    issue_tile(t + 2);  // into the stage that held tile t-1
-    const unsigned char* S = smem + (t % FA_NSTAGE) * FA_STAGE;
-    const int kb0 = t * FA_KT;
 
-    // ---- S^T[key][query] = K Q^T: 2 key blocks x 2 query blocks x 12 k steps
-    f32x16 sacc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int s = 0; s < 12; ++s) {
-        const u32x4 kf = *(const u32x4*)(S + (s < 8 ? kc_off[s] : kr_off[s - 8]) + kb * 32 * (s < 8 ? 256 : 128));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (s == 0)
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sacc[kb][qb]) : "v"(kf), "v"(qf[qb][s]));
-          else
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc[kb][qb]) : "v"(kf), "v"(qf[qb][s]));
-        }
-      }
-    }
-    // wait states before VALU reads the MFMA results
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  f32x16 sA[2][2], sB[2][2];  // S^T [key block][query block] of two consecutive tiles
+  u32x4 pA[4][2], pB[4][2];   // P^T [key step][query block] of two consecutive tiles
 
-    // ---- online softmax per query (log2 domain).  Lane holds, for query l32
-    // of block qb, keys kb0 + 32 kb + 8 (i/4) + 4 hi + i%4.
-    u32x4 pf[4][2];  // P^T fragments [key step][query block]
-    if (kb0 + FA_KT - 1 > qpos0) {
-      // a tile on the diagonal: key kb0 + 32 kb + 8 (i/4) + 4 hi + i%4 is
+  // One pipeline step for tile t, all in one instruction stream:
+  //   MFMA: S^T of tile t+1 (48, if QK) then O^T += V^T P^T of tile t-1 (32, if PV)
+  //   VALU: softmax of tile t (mask, max, running max, exp, P^T pack, row sum),
+  //         one slot after each MFMA
+  // then the accumulator rescale for tile t's running max.  Tile t+1's k rows
+  // and tile t-1's v rows are in LDS.
+  auto step = [&](int t, f32x16 (&sc)[2][2], f32x16 (&sn)[2][2], u32x4 (&pc)[4][2], u32x4 (&pp)[4][2]) {
+    // tile t+3's loads go out one every 8 MFMAs (a burst would stall the wave
+    // on the memory pipeline)
+    const TileSrc ts = tile_src(t + 3);
+    const uint32_t kq = smem_addr + ((t + 1) % FA_NK) * FA_KSTAGE + kx;
+    const uint32_t rq = smem_addr + ((t + 1) % FA_NK) * FA_KSTAGE + rx;
+    const uint32_t vq = smem_addr + FA_VBASE + ((t + FA_NV - 1) % FA_NV) * FA_VSTAGE + vx;
+    if (t * FA_KT + FA_KT - 1 > qpos0) {
+      // a tile on the diagonal: key t*64 + 32 kb + 8 (i/4) + 4 hi + i%4 is
       // masked for query qpos0 + 32 qb + l32 when 8 (i/4) + i%4 exceeds thr
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int thr = qpos0 + 32 * qb + l32 - kb0 - 32 * kb - 4 * hi;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) > thr) sacc[kb][qb][i] = -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+          fa_causal_mask(sc[kb][qb], qpos0 + 32 * qb + l32 - t * FA_KT - 32 * kb - 4 * hi);
     }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
-      // a query's first tile always holds key 0, so mt is finite there and the
-      // rescale below (alpha = 0) also initialises m_run
-      const float mt = pair_max32(mx) * scale_log2;
-      if (__any(mt > m_run[qb] + FA_SLACK)) {
-        const float mn = fmaxf(m_run[qb], mt);
-        const float alpha = exp2f(m_run[qb] - mn);
-        l_run[qb] *= alpha;
-        m_run[qb] = mn;
-        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-        for (int d = 0; d < 4; ++d) fa_scale_tuple(acc[d][qb], alpha);
-        asm volatile("s_nop 4" ::: "memory");
-      }
-      const float neg_m = -m_run[qb];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * h2 + 2 * e;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][i], scale_log2, neg_m));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][i + 1], scale_log2, neg_m));
-            pf[2 * kb + h2][qb][e] = pack_bf16x2(e0, e1);
-            l_run[qb] += e0 + e1;
-          }
-    }
-
-    // ---- O^T[dim][query] += V^T[dim][key] P^T[key][query]
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const unsigned char* vb = S + v_off[d] + ks * 16 * 256;
+    // MFMA order: 44 units of two MFMAs (query blocks 0, 1), interleaving
+    // S^T of tile t+1 with O^T += V^T P^T of tile t-1 so the transposing
+    // value reads and the key reads share the LDS evenly (fa_unit_kind).
+    constexpr int NF = 40, NM = 88, NSTEP = NM;
+    constexpr int FW = 3;  // fragments read ahead
+    u32x4 fr[FW + 1];
+    auto load_frag = [&](auto G) -> u32x4 {
+      constexpr int u = fa_load_unit(decltype(G)::value);
+      if constexpr (fa_unit_kind(u) == 'P') {
+        constexpr int ks = u / 11, d = (u % 11 - 1) / 2;
+        const uint32_t vb = (vq ^ (64 * d)) + ks * 16 * 256;
         const u32x2 lo = fa_tr16(vb), hv = fa_tr16(vb + 8 * 256);
-        const u32x4 vf = {lo[0], lo[1], hv[0], hv[1]};
+        return u32x4{lo[0], lo[1], hv[0], hv[1]};
+      } else {
+        constexpr int f = fa_unit_q(u), kb = f / 12, s = f % 12;
+        if constexpr (s < 8)
+          return fa_lds16((kq ^ (32 * s)) + kb * 32 * 256);
+        else
+          return fa_lds16((rq ^ (32 * (s - 8))) + kb * 32 * 128);
+      }
+    };
+    float mx[2] = {-INFINITY, -INFINITY}, mh[2], alpha[2], xa, xb, ea, eb;
+    bool need[2];
+    static_for<FW>([&](auto G) { fr[decltype(G)::value] = load_frag(G); });
+    static_for<NSTEP>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int u = j / 2, qb = j % 2;
+      constexpr char kind = fa_unit_kind(u);
+      if constexpr (kind != 'O' && qb == 0 && fa_unit_load(u) + FW < NF)
+        fr[(fa_unit_load(u) + FW) % (FW + 1)] = load_frag(std::integral_constant<int, fa_unit_load(u) + FW>{});
+      if constexpr (j % 8 == 4 && j / 8 < FA_DMA) dma_one(ts, j / 8);
+      if constexpr (kind == 'P') {
+        constexpr int ks = u / 11, d = (u % 11 - 1) / 2;
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+            : "+a"(acc[d][qb]) : "v"(fr[fa_unit_load(u) % (FW + 1)]), "v"(pp[ks][qb]));
+      } else if constexpr (kind == 'O') {
+        constexpr int ks = u / 11;
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc_l[qb]) : "v"(ones), "v"(pp[ks][qb]));
+      } else {
+        constexpr int f = fa_unit_q(u), kb = f / 12, s = f % 12;
+        if constexpr (s == 0)
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+              : "=v"(sn[kb][qb]) : "v"(fr[fa_unit_load(u) % (FW + 1)]), "a"(qf[qb][s]));
+        else
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+              : "+v"(sn[kb][qb]) : "v"(fr[fa_unit_load(u) % (FW + 1)]), "a"(qf[qb][s]));
+      }
+      // Softmax of tile t, one slot after each MFMA.  No instruction in a slot
+      // uses a result from the same slot (the wave issues in order, so a wait
+      // on a VALU result would also hold up the next MFMA).
+      if constexpr (j < 16) {  // row max over the tile, two values per query block per slot
+        constexpr int kb = j >> 3, i = 2 * (j & 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) mx[qb] = fa_max3(mx[qb], sc[kb][qb][i], sc[kb][qb][i + 1]);
+      } else if constexpr (j == 16) {  // the other half of each query's keys is in lane l ^ 32
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[qb]), __float_as_uint(mx[qb]), false, false);
+          mx[qb] = __uint_as_float(r[0]);
+          mh[qb] = __uint_as_float(r[1]);
+        }
+      } else if constexpr (j == 17) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) mx[qb] = fa_max3(mx[qb], mh[qb], mh[qb]);
+      } else if constexpr (j == 18) {  // tile max in log2 units; the raise threshold
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          mx[qb] *= scale_log2;
+          mh[qb] = m_run[qb] + FA_SLACK;
+        }
+      } else if constexpr (j == 19) {
+        // running max, raised only when the tile max exceeds it by more than
+        // FA_SLACK (p <= 2^8 stays exact in fp32); a query's first tile always
+        // holds key 0, so there the tile max is finite and alpha = 0
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) need[qb] = __any(mx[qb] > mh[qb]);
+      } else if constexpr (j == 20) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) mx[qb] = fa_max3(mx[qb], m_run[qb], m_run[qb]);
+      } else if constexpr (j == 21) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) mh[qb] = need[qb] ? mx[qb] : m_run[qb];  // new running max
+      } else if constexpr (j == 22) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) alpha[qb] = m_run[qb] - mh[qb];
+      }
+      if constexpr (j == 23) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          alpha[qb] = __builtin_amdgcn_exp2f(alpha[qb]);
+          m_run[qb] = mh[qb];
+        }
+      }
+      // pair k of scores: x = s * scale - m at slot 23 + 2k, exp at 24 + 2k,
+      // bf16 pack into P^T at 25 + 2k
+      if constexpr (j >= 25 && (j - 25) % 2 == 0 && (j - 25) / 2 < 32) {
+        constexpr int k = (j - 25) / 2, qb = k >> 4, kb = (k >> 3) & 1, h2 = (k >> 2) & 1, e = k & 3;
+        pc[2 * kb + h2][qb][e] = pack_bf16x2(ea, eb);
+      }
+      if constexpr (j >= 24 && (j - 24) % 2 == 0 && (j - 24) / 2 < 32) {
+        ea = __builtin_amdgcn_exp2f(xa);
+        eb = __builtin_amdgcn_exp2f(xb);
+      }
+      if constexpr (j >= 23 && (j - 23) % 2 == 0 && (j - 23) / 2 < 32) {
+        constexpr int k = (j - 23) / 2, qb = k >> 4, kb = (k >> 3) & 1, h2 = (k >> 2) & 1, e = k & 3;
+        constexpr int i = 8 * h2 + 2 * e;
+        xa = __builtin_fmaf(sc[kb][qb][i], scale_log2, -mh[qb]);
+        xb = __builtin_fmaf(sc[kb][qb][i + 1], scale_log2, -mh[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // the accumulator now holds tiles <= t-1 at the old running max
+    if (need[0] || need[1]) {
+      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        if (need[qb]) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) fa_scale_tuple(acc[d][qb], alpha[qb]);
+          fa_scale_tuple(acc_l[qb], alpha[qb]);
+        }
+      asm volatile("s_nop 4" ::: "memory");
+    }
+  };
+  // O^T += V^T P^T for the wave's last tile (its v rows are still in LDS)
+  auto pv_last = [&](int t, u32x4 (&pc)[4][2]) {
+    const uint32_t vq = smem_addr + FA_VBASE + (t % FA_NV) * FA_VSTAGE + vx;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int ks = g >> 2, d = g & 3;
+      const uint32_t vb = (vq ^ (64 * d)) + ks * 16 * 256;
+      const u32x2 lo = fa_tr16(vb), hv = fa_tr16(vb + 8 * 256);
+      const u32x4 vf = {lo[0], lo[1], hv[0], hv[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[d][qb]) : "v"(vf), "v"(pc[ks][qb]));
+      if (d == 3) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[d][qb]) : "v"(vf), "v"(pf[ks][qb]));
+          asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc_l[qb]) : "v"(ones), "v"(pc[ks][qb]));
       }
     }
-  }
-  for (; t < ntiles; ++t) {
+  };
+  // every wave waits for tile t+1, then the stages of tiles t-2 (k rows) and
+  // t-3 (v rows) take tile t+3
+  auto sync = [&]() {
     fa_wait_vmcnt<FA_DMA>();
     __syncthreads();
-    issue_tile(t + 2);
+  };
+
+  // prologue: S^T of tile 0.  The first step's value product runs on a
+  // zeroed "tile -1" (the v stage tile 4 takes later) with P^T = 0.
+#pragma unroll
+  for (int i = 0; i < FA_VSTAGE / (256 * 16); ++i)
+    *(u32x4*)(smem + FA_VBASE + (FA_NV - 1) * FA_VSTAGE + (i * 256 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) pB[k][qb] = u32x4{0u, 0u, 0u, 0u};
+  fa_wait_vmcnt<2 * FA_DMA>();
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < 24; ++f) {
+    const int kb = f / 12, s = f % 12;
+    const u32x4 kf = s < 8 ? fa_lds16(((smem_addr + kx) ^ (32 * s)) + kb * 32 * 256)
+                           : fa_lds16(((smem_addr + rx) ^ (32 * (s - 8))) + kb * 32 * 128);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (s == 0)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sA[kb][qb]) : "v"(kf), "a"(qf[qb][s]));
+      else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sA[kb][qb]) : "v"(kf), "a"(qf[qb][s]));
+    }
+  }
+  // wait states before VALU reads the MFMA results
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // Tile steps run in pairs (the two score and P^T buffers swap roles), so a
+  // wave with an odd tile count runs one more, all of whose keys are after its
+  // queries: fully masked, it adds nothing.  Every wave passes the same number
+  // of barriers, one per tile step up to ntiles rounded up to even.
+  const int nt_even = (nt_wave + 1) & ~1, nt_all = (ntiles + 1) & ~1;
+  int t = 0;
+  for (; t < nt_even; t += 2) {
+    sync();
+    step(t, sA, sB, pA, pB);
+    sync();
+    step(t + 1, sB, sA, pB, pA);
+  }
+  pv_last(t - 1, pB);
+  for (; t < nt_all; ++t) {
+    sync();
+    issue_tile(t + 3);
   }
   fa_wait_vmcnt<0>();  // tiles past the end still write LDS: drain them
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[2][0]),
-                 "+a"(acc[2][1]), "+a"(acc[3][0]), "+a"(acc[3][1]));
+                 "+a"(acc[2][1]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc_l[0]), "+a"(acc_l[1]));
 
   // ---- out[t][head][:] = O^T[:, t] / l.  Lane (l32, hi), tuple (d, qb),
   // register 4g + e: dim 32 d + 8 g + 4 hi + e of query 32 qb + l32; lanes l
@@ -307,7 +513,7 @@ void fa_bf16_kernel(FaArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tq = q0 + FA_QW * wave + 32 * qb + l32;
-    const float inv = 1.f / pair_sum32(l_run[qb]);
+    const float inv = 1.f / acc_l[qb][0];
     if (tq < a.L) {
       bf16* o = (bf16*)a.out + (((int64_t)b * a.L + tq) * H + head) * FA_DH;
 #pragma unroll
