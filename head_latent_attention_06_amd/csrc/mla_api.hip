@@ -262,18 +262,24 @@ AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_lat
   return a;
 }
 
-// Attention + merge + W^UV for rows whose absorbed queries are in q_abs.
-mla_status attend(const mla_config* c, bool bf16, AttnArgs a, int32_t* plan, int64_t max_items, int32_t target,
-                  bool need_merge, void* part_o, float* part_ml, void* o_lat, const void* w_uv, void* out,
-                  hipStream_t st, void* ev0, void* ev1) {
-  const int64_t rows = (int64_t)a.B * a.s_q;
+// The plan / split-partial fields of an attention call.
+void set_plan(AttnArgs& a, int32_t* plan, int64_t max_items, void* part_o, float* part_ml, void* o_lat) {
   a.o_lat = o_lat;
+  a.plan = plan;
+  a.max_items = (int32_t)max_items;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+}
+
+// Attention + merge + W^UV for rows whose absorbed queries are in q_abs (a
+// carries the plan fields; plan_built: the plan is already on the stream).
+mla_status attend(const mla_config* c, bool bf16, const AttnArgs& a, int32_t target, bool plan_built,
+                  bool need_merge, const void* w_uv, void* out, hipStream_t st, void* ev0, void* ev1) {
+  const int64_t rows = (int64_t)a.B * a.s_q;
+  const void* o_lat = a.o_lat;
   if (bf16) {
-    a.plan = plan;
-    a.max_items = (int32_t)max_items;
-    a.part_o = part_o;
-    a.part_ml = part_ml;
-    MLA_HIP(launch_attn_plan(a, plan, target, MIN_CHUNK, max_chunk_keys(c) / 32 * 32, st));
+    if (!plan_built)
+      MLA_HIP(launch_attn_plan(a, const_cast<int32_t*>(a.plan), target, MIN_CHUNK, max_chunk_keys(c) / 32 * 32, st));
     if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
     MLA_HIP(launch_attn_bf16(a, st));
     if (ev1) MLA_HIP(hipEventRecord((hipEvent_t)ev1, st));
@@ -468,8 +474,8 @@ mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache
   AttnArgs a = attn_args(cfg, cache, p.q_abs, row, (const unsigned char*)p.q_abs + cfg->d_c * e, row, nullptr,
                          (int32_t)kv_end, (int32_t)kv_end, B, L);
   a.longest_first = 1;
-  return attend(cfg, bf16, a, p.plan, p.max_items, 0, p.split, p.part_o, p.part_ml, p.o_lat, w->w_uv, out, st,
-                attn_start, attn_stop);
+  set_plan(a, p.plan, p.max_items, p.part_o, p.part_ml, p.o_lat);
+  return attend(cfg, bf16, a, 0, false, p.split, w->w_uv, out, st, attn_start, attn_stop);
 }
 
 mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t s_q, int32_t max_kv_len,
@@ -519,15 +525,21 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
   if (need > ws_bytes) return MLA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int rows = B * s_q, H = cfg->n_heads;
-  // absorption: q_lat[t, i, :] = W_i^UK^T q^C[t, i]  (q^R is read from q_pe directly)
-  if ((s = launch_gemm(bf16, gemm(q_nope, (int64_t)H * cfg->d_head, cfg->d_head, w_uk, cfg->d_c,
-                                  (int64_t)cfg->d_head * cfg->d_c, d.q_lat, (int64_t)H * cfg->d_c, cfg->d_c, rows,
-                                  cfg->d_c, cfg->d_head, H, true, bf16), st)) != MLA_OK)
-    return s;
   AttnArgs a = attn_args(cfg, cache, d.q_lat, cfg->d_c, q_pe, cfg->d_rope, kv_lens, 0, max_kv_len, B, s_q);
   a.longest_first = 0;
-  return attend(cfg, bf16, a, d.plan, d.max_items, DECODE_TARGET_ITEMS, true, d.part_o, d.part_ml, d.o_lat, w_uv,
-                out, st, attn_start, attn_stop);
+  set_plan(a, d.plan, d.max_items, d.part_o, d.part_ml, d.o_lat);
+  // absorption: q_lat[t, i, :] = W_i^UK^T q^C[t, i]  (q^R is read from q_pe
+  // directly); the split plan is built by one extra workgroup of that launch
+  const GemmArgs absorb = gemm(q_nope, (int64_t)H * cfg->d_head, cfg->d_head, w_uk, cfg->d_c,
+                               (int64_t)cfg->d_head * cfg->d_c, d.q_lat, (int64_t)H * cfg->d_c, cfg->d_c, rows,
+                               cfg->d_c, cfg->d_head, H, true, bf16);
+  if (bf16) {
+    PlanJob pj{a, d.plan, DECODE_TARGET_ITEMS, MIN_CHUNK, max_chunk_keys(cfg) / 32 * 32};
+    MLA_HIP(launch_gemm_bf16_plan(absorb, pj, st));
+  } else if ((s = launch_gemm(bf16, absorb, st)) != MLA_OK) {
+    return s;
+  }
+  return attend(cfg, bf16, a, DECODE_TARGET_ITEMS, true, true, w_uv, out, st, attn_start, attn_stop);
 }
 
 }  // extern "C"

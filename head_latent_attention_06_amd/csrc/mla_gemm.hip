@@ -19,6 +19,7 @@
 // multiple of 64.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "mla_plan.h"
 
 namespace mla {
 namespace {
@@ -237,8 +238,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // output tile is staged in LDS and written with 16-byte stores.
 constexpr int SM_BM = 64, SM_BN = 64;
 
-template <bool B_KN, int KMAX>
-__global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g) {
+template <bool B_KN, int KMAX, bool PLAN>
+__global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g, PlanJob pj) {
+  if constexpr (PLAN) {
+    // columns past the batch pad the grid width to a multiple of 8 (so each
+    // batch entry keeps its XCD); the first of them builds the attention plan
+    if ((int)blockIdx.x >= g.batch) {
+      if ((int)blockIdx.x == g.batch && blockIdx.y == 0)
+        plan_body(pj.a, pj.plan, pj.target_items, pj.min_chunk, pj.max_chunk);
+      return;
+    }
+  }
   constexpr int RS = KMAX * 2 + 16;  // LDS row stride in bytes (16-byte pad: conflict-free fragment reads)
   __shared__ __attribute__((aligned(16))) unsigned char sa[SM_BM * RS];
   __shared__ __attribute__((aligned(16))) unsigned char sb[SM_BN * RS];
@@ -334,21 +344,33 @@ __global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g) {
 
 }  // namespace
 
+namespace {
+bool smallm_form(const GemmArgs& g) {
+  return g.M <= SM_BM && g.K <= 512 && g.K % 64 == 0 && g.N % 8 == 0 && g.out_bf16 && !g.B2;
+}
+
+template <bool PLAN>
+void launch_smallm(const GemmArgs& g, const PlanJob& pj, hipStream_t st) {
+  const unsigned gx = PLAN ? (unsigned)((g.batch + 1 + 7) / 8 * 8) : (unsigned)g.batch;
+  dim3 grid(gx, (unsigned)((g.N + SM_BN - 1) / SM_BN));
+  if (g.K <= 128) {
+    if (g.b_kn)
+      hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 128, PLAN>), grid, dim3(256), 0, st, g, pj);
+    else
+      hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 128, PLAN>), grid, dim3(256), 0, st, g, pj);
+  } else {
+    if (g.b_kn)
+      hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 512, PLAN>), grid, dim3(256), 0, st, g, pj);
+    else
+      hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 512, PLAN>), grid, dim3(256), 0, st, g, pj);
+  }
+}
+}  // namespace
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  if (g.M <= SM_BM && g.K <= 512 && g.K % 64 == 0 && g.N % 8 == 0 && g.out_bf16 && !g.B2) {
-    dim3 grid((unsigned)g.batch, (unsigned)((g.N + SM_BN - 1) / SM_BN));
-    if (g.K <= 128) {
-      if (g.b_kn)
-        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 128>), grid, dim3(256), 0, st, g);
-      else
-        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 128>), grid, dim3(256), 0, st, g);
-    } else {
-      if (g.b_kn)
-        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 512>), grid, dim3(256), 0, st, g);
-      else
-        hipLaunchKernelGGL((gemm_smallm_bf16_kernel<false, 512>), grid, dim3(256), 0, st, g);
-    }
+  if (smallm_form(g)) {
+    launch_smallm<false>(g, PlanJob{}, st);
     return hipGetLastError();
   }
   const unsigned tiles = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
@@ -365,6 +387,16 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
       hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, dim3(256), 0, st, g);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_plan(const GemmArgs& g, const PlanJob& p, hipStream_t st) {
+  if (g.M > 0 && g.N > 0 && g.batch > 0 && smallm_form(g)) {
+    launch_smallm<true>(g, p, st);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_attn_plan(p.a, p.plan, p.target_items, p.min_chunk, p.max_chunk, st);
+  if (e != hipSuccess) return e;
+  return launch_gemm_bf16(g, st);
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t st) {

@@ -67,6 +67,16 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+
+// A GEMM and, in one extra workgroup of the same launch, the attention work
+// plan (launch_attn_plan's job); falls back to two launches for GEMM shapes
+// without that form.
+struct PlanJob {
+  AttnArgs a;
+  int32_t* plan;
+  int32_t target_items, min_chunk, max_chunk;
+};
+hipError_t launch_gemm_bf16_plan(const GemmArgs& g, const PlanJob& p, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t st);
 
 // Cache append: row i -> [RMSNorm(ckv[i]) ; RoPE(kr[i], pos)] into its page slot.
