@@ -31,6 +31,15 @@ design notes of the repository):
     theta_p = base^(-2p/d_rope) (the RoPE frequency formula quoted on the
     hnwysp.cn digest, section 4.3), base 10000, positions counted from 0.
   * Output stops at o = [o_1; ...; o_{n_h}]; W^O is not applied.
+  * YaRN (optional, the long-context extension of the notes page, section
+    三(二)3 "长上下文扩展": s = 40, alpha = 1, beta = 32, factor 0.1 ln s + 1,
+    with the method's meaning taken from the YaRN paper the page points to):
+    every RoPE frequency theta_p becomes (1 - g) theta_p / s + g theta_p,
+    where g ramps from 0 to 1 as the pair's rotations over the original
+    context, r_p = orig_ctx theta_p / (2 pi), go from alpha to beta; and every
+    attention logit is multiplied by (0.1 ln s + 1)^2 (YaRN applies the square
+    root of that temperature to both q and k).  The same frequencies rotate
+    q^R and k^R, so scores still depend only on relative positions.
   * Decode: the step's s_q new tokens are already cached; query s of a
     sequence with kv_len cached rows sits at position kv_len - s_q + s and
     attends to rows j <= that position.
@@ -62,16 +71,36 @@ def rope_frequencies(d_rope: int, base: float) -> np.ndarray:
     return np.power(F64(base), -2.0 * p / d_rope)
 
 
-def rope(x, pos, base: float) -> np.ndarray:
+def yarn_frequencies(d_rope: int, base: float, yarn) -> np.ndarray:
+    """YaRN frequencies: theta'_p = (1 - g_p) theta_p / s + g_p theta_p.
+
+    ``yarn`` = dict(s=..., alpha=..., beta=..., orig_ctx=...).  r_p =
+    orig_ctx * theta_p / (2 pi) counts the pair's rotations over the original
+    context; g_p = 0 for r_p < alpha (pure interpolation by s), 1 for
+    r_p > beta (unchanged), linear in between.
+    """
+    theta = rope_frequencies(d_rope, base)
+    r = F64(yarn["orig_ctx"]) * theta / (2.0 * np.pi)
+    g = np.clip((r - F64(yarn["alpha"])) / (F64(yarn["beta"]) - F64(yarn["alpha"])), 0.0, 1.0)
+    return (1.0 - g) * theta / F64(yarn["s"]) + g * theta
+
+
+def yarn_logit_factor(s: float) -> float:
+    """Multiplier of every attention logit under YaRN: (0.1 ln s + 1)^2."""
+    return float((0.1 * np.log(F64(s)) + 1.0) ** 2)
+
+
+def rope(x, pos, base: float, yarn=None) -> np.ndarray:
     """Rotate each adjacent pair of the last axis by pos * theta_p.
 
     Section 一(一)3 gives R_m as a block-diagonal matrix of 2x2 rotations
     [[cos m.theta, -sin m.theta], [sin m.theta, cos m.theta]].  ``x`` is
-    [..., d_rope]; ``pos`` broadcasts against x's leading axes.
+    [..., d_rope]; ``pos`` broadcasts against x's leading axes.  With ``yarn``
+    the frequencies are the YaRN ones.
     """
     x = _f64(x)
     d = x.shape[-1]
-    theta = rope_frequencies(d, base)
+    theta = rope_frequencies(d, base) if yarn is None else yarn_frequencies(d, base, yarn)
     ang = _f64(pos)[..., None] * theta            # [..., d/2]
     c, s = np.cos(ang), np.sin(ang)
     x0, x1 = x[..., 0::2], x[..., 1::2]
@@ -90,7 +119,7 @@ def split_heads(x, n_heads: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Projections (steps (1)-(3), (5), (7))
 # ---------------------------------------------------------------------------
-def query_path(h, w_dq, g_q, w_uq, w_qr, pos, n_heads: int, eps: float, base: float):
+def query_path(h, w_dq, g_q, w_uq, w_qr, pos, n_heads: int, eps: float, base: float, yarn=None):
     """Steps (1)-(3): c^Q = RMSNorm(W^DQ h); q^C = W^UQ c^Q; q^R = RoPE(W^QR c^Q).
 
     h: [T, d]; pos: [T].  Returns q^C [T, H, d_h] and q^R [T, H, d_rope].
@@ -99,11 +128,11 @@ def query_path(h, w_dq, g_q, w_uq, w_qr, pos, n_heads: int, eps: float, base: fl
     c_q = rms_norm(h @ _f64(w_dq).T, g_q, eps)
     q_c = split_heads(c_q @ _f64(w_uq).T, n_heads)
     q_r_raw = split_heads(c_q @ _f64(w_qr).T, n_heads)
-    q_r = rope(q_r_raw, _f64(pos)[:, None], base)
+    q_r = rope(q_r_raw, _f64(pos)[:, None], base, yarn)
     return q_c, q_r
 
 
-def latent_rows(h, w_dkv, g_kv, w_kr, pos, eps: float, base: float):
+def latent_rows(h, w_dkv, g_kv, w_kr, pos, eps: float, base: float, yarn=None):
     """Steps (5) and (7): c^KV = RMSNorm(W^DKV h) and k^R = RoPE(W^KR h).
 
     These two vectors are all that is cached per token (section 一(一)3, end of
@@ -111,13 +140,13 @@ def latent_rows(h, w_dkv, g_kv, w_kr, pos, eps: float, base: float):
     """
     h = _f64(h)
     c = rms_norm(h @ _f64(w_dkv).T, g_kv, eps)
-    k_r = rope(h @ _f64(w_kr).T, pos, base)
+    k_r = rope(h @ _f64(w_kr).T, pos, base, yarn)
     return c, k_r
 
 
-def cache_row(c_raw, k_raw, g_kv, pos, eps: float, base: float) -> np.ndarray:
+def cache_row(c_raw, k_raw, g_kv, pos, eps: float, base: float, yarn=None) -> np.ndarray:
     """One cached row from the raw projections: [RMSNorm(c_raw) ; RoPE(k_raw, pos)]."""
-    return np.concatenate([rms_norm(c_raw, g_kv, eps), rope(k_raw, pos, base)], axis=-1)
+    return np.concatenate([rms_norm(c_raw, g_kv, eps), rope(k_raw, pos, base, yarn)], axis=-1)
 
 
 # ---------------------------------------------------------------------------
@@ -240,25 +269,28 @@ def decode(rows_per_seq, kv_lens, s_q: int, q_nope, q_pe, w_uk, w_uv, d_c: int, 
 
 
 def prefill(h, w, n_heads: int, eps: float, base: float, scale: float, start_pos: int = 0,
-            past_rows=None, tokens=None, heads=None):
+            past_rows=None, tokens=None, heads=None, yarn=None):
     """Steps (1)-(10) for one sequence: h [L, d] holds tokens start_pos .. start_pos+L-1.
 
     ``past_rows`` [start_pos, d_c + d_rope] are the rows already cached for
     earlier positions.  Returns (o [len(tokens), len(heads), d_h], new_rows
     [L, d_c + d_rope]).  ``tokens`` selects which new tokens' outputs to compute.
+    With ``yarn`` the RoPE frequencies are YaRN's and the logits are scaled by
+    yarn_logit_factor(s) on top of ``scale``.
     """
     h = _f64(h)
     L = h.shape[0]
     pos = start_pos + np.arange(L)
     d_c = np.asarray(w["w_dkv"]).shape[0]
-    c, k_r = latent_rows(h, w["w_dkv"], w["g_kv"], w["w_kr"], pos, eps, base)
+    c, k_r = latent_rows(h, w["w_dkv"], w["g_kv"], w["w_kr"], pos, eps, base, yarn)
     new_rows = np.concatenate([c, k_r], axis=1)
     rows = new_rows if past_rows is None or start_pos == 0 else np.concatenate([_f64(past_rows), new_rows])
     tokens = np.arange(L) if tokens is None else np.asarray(tokens)
     q_c, q_r = query_path(h[tokens], w["w_dq"], w["g_q"], w["w_uq"], w["w_qr"], pos[tokens],
-                          n_heads, eps, base)
+                          n_heads, eps, base, yarn)
+    eff_scale = scale if yarn is None else scale * yarn_logit_factor(yarn["s"])
     o = explicit_attention(q_c, q_r, rows[:, :d_c], rows[:, d_c:], w["w_uk"], w["w_uv"],
-                           pos[tokens], scale, heads=heads)
+                           pos[tokens], eff_scale, heads=heads)
     return o, new_rows
 
 

@@ -372,3 +372,102 @@ def test_prefill_with_past_rows_matches_whole():
     o2, rows2 = om.prefill(h[4:], w, H, eps, base, scale, start_pos=4, past_rows=rows_all[:4])
     assert _rel(rows2, rows_all[4:]) <= 1e-14
     assert _rel(o2, o_all[4:]) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# YaRN (the long-context extension; frequencies and logit factor)
+# ---------------------------------------------------------------------------
+def _yarn_page():
+    g = json.load(open(GOLDEN))["yarn_hyperparameters"]
+    return dict(s=g["s"], alpha=g["alpha"], beta=g["beta"], orig_ctx=g["orig_ctx"]), g
+
+
+def test_yarn_s1_is_plain_rope():
+    y = dict(s=1.0, alpha=1.0, beta=32.0, orig_ctx=4096)
+    assert np.allclose(om.yarn_frequencies(64, 10000.0, y), om.rope_frequencies(64, 10000.0), rtol=1e-15, atol=0)
+    assert om.yarn_logit_factor(1.0) == 1.0
+    r = np.random.default_rng(40)
+    x = r.standard_normal((3, 64))
+    assert np.allclose(om.rope(x, np.array([0, 5, 70000]), 10000.0, y), om.rope(x, np.array([0, 5, 70000]), 10000.0),
+                       rtol=0, atol=1e-9)
+
+
+def test_yarn_ramp_closed_forms():
+    """One pair with theta = 1: its rotations over the original context are
+    orig_ctx / (2 pi), so choosing orig_ctx puts it at alpha, beta or halfway."""
+    s, a, b = 40.0, 1.0, 32.0
+    for ctx, want in [(2 * math.pi * a, 1.0 / s), (2 * math.pi * b, 1.0), (2 * math.pi * (a + b) / 2, (1.0 / s + 1.0) / 2),
+                      (2 * math.pi * 0.25, 1.0 / s), (2 * math.pi * 1000.0, 1.0)]:
+        th = om.yarn_frequencies(2, 10000.0, dict(s=s, alpha=a, beta=b, orig_ctx=ctx))
+        assert abs(th[0] - want) <= 1e-15, (ctx, th[0], want)
+
+
+def test_yarn_page_values_limits_and_monotone():
+    """With the page's values and the V3 RoPE width: the fastest pair (theta = 1,
+    ~652 rotations over 4K) is unchanged, the slowest (< 1 rotation) is divided
+    by s, and the ratio theta'/theta falls monotonically between."""
+    y, _ = _yarn_page()
+    base = om.rope_frequencies(64, 10000.0)
+    th = om.yarn_frequencies(64, 10000.0, y)
+    assert th[0] == base[0] == 1.0
+    assert abs(th[31] - base[31] / y["s"]) <= 1e-18
+    ratio = th / base
+    assert np.all(np.diff(ratio) <= 1e-15) and ratio.min() >= 1.0 / y["s"] - 1e-15 and ratio.max() <= 1.0
+    inner = (ratio > 1.0 / y["s"] + 1e-12) & (ratio < 1.0 - 1e-12)
+    assert inner.sum() >= 3  # the ramp is populated
+
+
+def test_yarn_low_frequency_pairs_interpolate_positions():
+    """A pair left fully interpolated (g = 0) rotates at position s*m exactly as
+    plain RoPE does at m: the context extension of YaRN's low frequencies."""
+    y, _ = _yarn_page()
+    base = om.rope_frequencies(64, 10000.0)
+    th = om.yarn_frequencies(64, 10000.0, y)
+    low = np.where(np.abs(th - base / y["s"]) <= 1e-18)[0]
+    assert len(low) >= 4
+    r = np.random.default_rng(41)
+    x = r.standard_normal(64)
+    m = np.array([3, 100, 4000])
+    a = om.rope(np.tile(x, (3, 1)), m * y["s"], 10000.0, y)
+    b = om.rope(np.tile(x, (3, 1)), m, 10000.0)
+    for p in low:
+        assert np.allclose(a[:, 2 * p:2 * p + 2], b[:, 2 * p:2 * p + 2], atol=1e-9)
+
+
+def test_yarn_logit_factor_from_page():
+    """The page prints sqrt(t) = 0.1 ln s + 1; the logits are multiplied by its
+    square (YaRN applies that factor to both q and k)."""
+    y, g = _yarn_page()
+    c = g["factor_formula_coefficients"]
+    sqrt_t = c["a"] * math.log(y["s"]) + c["b"]
+    assert abs(om.yarn_logit_factor(y["s"]) - sqrt_t * sqrt_t) <= 1e-15
+    assert 1.87 < om.yarn_logit_factor(40.0) < 1.88
+
+
+def test_yarn_scores_depend_only_on_relative_position():
+    y, _ = _yarn_page()
+    r = np.random.default_rng(42)
+    H, dh, dr, dc, N = 2, 4, 8, 8, 9
+    q_c = r.standard_normal((3, H, dh))
+    q_raw = r.standard_normal((3, H, dr))
+    c = r.standard_normal((N, dc))
+    k_raw = r.standard_normal((N, dr))
+    w_uk = r.standard_normal((H * dh, dc))
+    w_uv = r.standard_normal((H * dh, dc))
+    q_pos = np.array([1, 5, 8])
+    outs = []
+    for shift in [0, 33, 90001]:
+        q_r = om.rope(q_raw, (q_pos + shift)[:, None], 10000.0, y)
+        k_r = om.rope(k_raw, np.arange(N) + shift, 10000.0, y)
+        outs.append(om.explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.4))
+    assert _rel(outs[1], outs[0]) <= 1e-9 and _rel(outs[2], outs[0]) <= 1e-9
+
+
+def test_yarn_prefill_s1_equals_plain_prefill():
+    s = mi.TINY
+    w = mi.weights(43, s, bf16=False)
+    h = mi.hidden(43, s, 1, 12, bf16=False)[0]
+    a, ra = om.prefill(h, w, s.n_heads, s.rms_eps, s.rope_base, s.scale)
+    b, rb = om.prefill(h, w, s.n_heads, s.rms_eps, s.rope_base, s.scale,
+                       yarn=dict(s=1.0, alpha=1.0, beta=32.0, orig_ctx=4096))
+    assert _rel(a, b) <= 1e-13 and _rel(ra, rb) <= 1e-13
