@@ -39,6 +39,9 @@ import mla_inputs as mi  # noqa: E402
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "MLA decode latent-KV GB/s + prefill TFLOP/s, % of MI355X roofline"
+# YaRN settings of the pages' long-context extension (used with --yarn)
+YARN = dict(yarn_s=40.0, yarn_alpha=1.0, yarn_beta=32.0, yarn_orig_ctx=4096)
+CFG_EXTRA: dict = {}
 
 
 class HipEvents:
@@ -74,7 +77,7 @@ def _up(a, dtype=torch.bfloat16):
 
 def decode_workload(copies: int):
     inp = mi.decode_inputs(2, mi.V3, mi.config_context_lens(2), 1)
-    cfg = mla.Config()
+    cfg = mla.Config(**CFG_EXTRA)
     bt, npages = mi.block_table(2, inp.kv_lens, cfg.page_size, shuffle=True)
     pool = torch.empty((npages, cfg.page_size, cfg.row), dtype=torch.bfloat16, device="cuda")
     flat = pool.view(-1, cfg.row)
@@ -147,7 +150,7 @@ def prefill_flops(s: mi.Shape, L: int, explicit: bool) -> dict:
 
 def run_prefill_bench(steps: int, warmup: int, form: int, L: int = 8192):
     s = mi.V3
-    cfg = mla.Config(prefill_form=form)
+    cfg = mla.Config(prefill_form=form, **CFG_EXTRA)
     w = {k: _up(v) for k, v in mi.weights(3, s).items()}
     h = _up(mi.hidden(3, s, 1, L))
     bt, npages = mi.block_table(3, [L], s.page_size, shuffle=True)
@@ -251,6 +254,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill workload (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--yarn", action="store_true",
+                    help="run both workloads with the YaRN long-context settings (s=40, alpha=1, beta=32, 4K window)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -263,6 +268,8 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.yarn:
+        CFG_EXTRA.update(YARN)
 
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill_summary(args)}), flush=True)
@@ -277,7 +284,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "MLA decode step, B=64 sequences x (4096 cached + 1 new) tokens, s_q=1, "
                                "n_h=128, d_h=128, d_c=512, d_h^R=64, 64-token pages, shuffled block table",
-                   "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)"},
+                   "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)",
+                   "yarn": bool(CFG_EXTRA)},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(d["attn_ms"], 5),

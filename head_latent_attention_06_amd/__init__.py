@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_RANGE, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
 MLA_F32, MLA_BF16 = 0, 1
 PREFILL_AUTO, PREFILL_ABSORBED, PREFILL_EXPLICIT = 0, 1, 2
-ABI_VERSION = 2  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
+ABI_VERSION = 3  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
 MLA_FLAG_BAD_PAGE, MLA_FLAG_BAD_POS, MLA_FLAG_BAD_LEN, MLA_FLAG_BAD_SEQ = 1, 2, 4, 8
 
 
@@ -34,7 +34,9 @@ class _Config(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("prefill_form", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("prefill_form", ctypes.c_int32),
+                ("yarn_s", ctypes.c_float), ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float),
+                ("yarn_orig_ctx", ctypes.c_int32)]
 
 
 class _Cache(ctypes.Structure):
@@ -105,6 +107,12 @@ class Config:
     rms_eps: float = 1e-6
     dtype: torch.dtype = torch.bfloat16
     prefill_form: int = PREFILL_AUTO  # PREFILL_AUTO / PREFILL_ABSORBED / PREFILL_EXPLICIT
+    # YaRN long-context extension; off while yarn_s <= 1 (the V3 values are s = 40,
+    # alpha = 1, beta = 32 over an original 4096-token window)
+    yarn_s: float = 0.0
+    yarn_alpha: float = 1.0
+    yarn_beta: float = 32.0
+    yarn_orig_ctx: int = 4096
 
     @property
     def row(self) -> int:
@@ -114,7 +122,8 @@ class Config:
         scale = self.softmax_scale if self.softmax_scale is not None else (self.d_head + self.d_rope) ** -0.5
         dt = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32}[self.dtype]
         return _Config(self.n_heads, self.d_head, self.d_rope, self.d_c, self.d_cq, self.d_model, self.page_size,
-                       scale, self.rope_base, self.rms_eps, dt, self.prefill_form)
+                       scale, self.rope_base, self.rms_eps, dt, self.prefill_form, self.yarn_s, self.yarn_alpha,
+                       self.yarn_beta, self.yarn_orig_ctx)
 
 
 @dataclass

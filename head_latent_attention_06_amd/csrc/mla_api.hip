@@ -2,6 +2,7 @@
 // carving and the launch sequence of each entry point.  Declarations and the
 // contract are in include/mla.h.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "mla.h"
@@ -30,6 +31,23 @@ struct Carve {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+RopeParams rope_params(const mla_config* c) {
+  RopeParams r{};
+  r.base = c->rope_base;
+  r.yarn_s = c->yarn_s > 1.f ? c->yarn_s : 0.f;
+  r.yarn_alpha = c->yarn_alpha;
+  r.yarn_beta = c->yarn_beta;
+  r.yarn_orig = c->yarn_orig_ctx;
+  return r;
+}
+
+// softmax_scale times the YaRN logit factor (0.1 ln s + 1)^2 when YaRN is on
+float logit_scale(const mla_config* c) {
+  if (!(c->yarn_s > 1.f)) return c->softmax_scale;
+  const double f = 0.1 * log((double)c->yarn_s) + 1.0;
+  return (float)((double)c->softmax_scale * f * f);
+}
+
 mla_status check_cfg(const mla_config* c, bool* bf16) {
   if (!c) return MLA_ERR_INVALID_ARG;
   if (c->n_heads <= 0 || c->d_head <= 0 || c->d_rope <= 0 || c->d_c <= 0 || c->d_cq <= 0 || c->d_model <= 0 ||
@@ -37,6 +55,7 @@ mla_status check_cfg(const mla_config* c, bool* bf16) {
     return MLA_ERR_INVALID_ARG;
   if (!(c->softmax_scale > 0.f) || !(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return MLA_ERR_INVALID_ARG;
   if (c->prefill_form < MLA_PREFILL_AUTO || c->prefill_form > MLA_PREFILL_EXPLICIT) return MLA_ERR_INVALID_ARG;
+  if (c->yarn_s > 1.f && !(c->yarn_beta > c->yarn_alpha && c->yarn_orig_ctx > 0)) return MLA_ERR_INVALID_ARG;
   if (c->page_size % 32 != 0 || (c->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
   if (c->dtype == MLA_BF16) {
     *bf16 = true;
@@ -213,7 +232,7 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
                               float* kv_raw, hipStream_t st) {
   const int64_t T = (int64_t)B * L;
   const int row = c->d_c + c->d_rope;
-  MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, c->rope_base, st));
+  MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, rope_params(c), st));
   GemmArgs g = gemm(h, c->d_model, 0, w->w_dkv, c->d_model, 0, kv_raw, row, 0, (int)T, row, c->d_model, 1, false,
                     false);
   g.B2 = w->w_kr;
@@ -231,7 +250,7 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   a.block_table = k->block_table; a.max_pages = k->max_pages_per_seq; a.page_size = c->page_size;
   a.err_flags = k->err_flags;
   a.d_c = c->d_c; a.d_rope = c->d_rope;
-  a.eps = c->rms_eps; a.rope_base = c->rope_base;
+  a.eps = c->rms_eps; a.rope = rope_params(c);
   a.bf16_cache = bf16 ? 1 : 0;
   MLA_HIP(launch_append(a, st));
   return MLA_OK;
@@ -258,7 +277,7 @@ AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_lat
   a.H = c->n_heads;
   a.d_c = c->d_c;
   a.d_rope = c->d_rope;
-  a.scale = c->softmax_scale;
+  a.scale = logit_scale(c);
   return a;
 }
 
@@ -324,7 +343,7 @@ mla_status prefill_explicit(const mla_config* c, const mla_kv_cache* k, const ml
   a.kr = (const unsigned char*)p.kvg + (size_t)c->d_c * 2;
   a.ld_kr = row;
   a.B = B; a.L = L; a.H = H; a.start_pos = start_pos; a.kv_end = kv_end;
-  a.scale = c->softmax_scale;
+  a.scale = logit_scale(c);
   a.out = out;
   if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
   MLA_HIP(launch_fa_bf16(a, st));
@@ -372,7 +391,7 @@ mla_status mla_cache_append(const mla_config* cfg, const mla_kv_cache* cache, co
   a.block_table = cache->block_table; a.max_pages = cache->max_pages_per_seq; a.page_size = cfg->page_size;
   a.err_flags = cache->err_flags;
   a.d_c = cfg->d_c; a.d_rope = cfg->d_rope;
-  a.eps = cfg->rms_eps; a.rope_base = cfg->rope_base;
+  a.eps = cfg->rms_eps; a.rope = rope_params(cfg);
   a.bf16_cache = bf16 ? 1 : 0;
   return launch_append(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -79,6 +79,15 @@ struct PlanJob {
 hipError_t launch_gemm_bf16_plan(const GemmArgs& g, const PlanJob& p, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t st);
 
+// RoPE frequencies theta_p = base^(-2p/d_rope), or with yarn_s > 1 the YaRN
+// ones: (1 - g) theta_p / yarn_s + g theta_p, g = clamp((r - alpha) / (beta -
+// alpha), 0, 1), r = yarn_orig * theta_p / (2 pi).
+struct RopeParams {
+  float base;
+  float yarn_s, yarn_alpha, yarn_beta;
+  int32_t yarn_orig;
+};
+
 // Cache append: row i -> [RMSNorm(ckv[i]) ; RoPE(kr[i], pos)] into its page slot.
 // seq_idx / pos may be null: then sequence = i / L and pos = start_pos + i % L.
 struct AppendArgs {
@@ -93,14 +102,15 @@ struct AppendArgs {
   const int32_t* block_table; int32_t max_pages, page_size;
   int32_t* err_flags;
   int32_t d_c, d_rope;
-  float eps, rope_base;
+  float eps;
+  RopeParams rope;
   int32_t bf16_cache;                // cache dtype is bf16 (else fp32)
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
 // cos / sin of pos * theta_p for positions start_pos .. start_pos + L - 1,
 // computed in double precision: out [L, d_rope/2, 2] fp32.
-hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, float base,
+hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, const RopeParams& rp,
                              hipStream_t st);
 
 // RMSNorm of fp32 rows into the storage dtype: out[r] = x[r] / rms(x[r]) * g.

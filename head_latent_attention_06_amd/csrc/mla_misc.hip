@@ -9,6 +9,11 @@
 //    theta_p = base^(-2p/d_rope) (the frequency formula of the hnwysp.cn
 //    digest, section 4.3).  Angles are formed and reduced in double precision:
 //    at position 131072 a float angle would already be off by ~1e-2 rad.
+//  * YaRN (section 三(二)3, the long-context extension, with the method's
+//    meaning from the YaRN paper it points to): when yarn_s > 1 each theta_p
+//    is interpolated by yarn_s where the pair turns fewer than alpha times
+//    over the original window, kept where it turns more than beta times, and
+//    ramped linearly between.
 //  * Only [c^KV ; k^R] is cached per token (end of section 一(一)3); token p
 //    of sequence b lives at slot p % page_size of page block_table[b][p / page_size].
 #include <math.h>
@@ -21,8 +26,13 @@ namespace {
 
 constexpr int FLAG_BAD_PAGE = 1, FLAG_BAD_POS = 2, FLAG_BAD_SEQ = 8;
 
-__device__ __forceinline__ void rope_cos_sin(int pos, int p, int d_rope, double base, float& c, float& s) {
-  const double theta = pow(base, -2.0 * (double)p / (double)d_rope);
+__device__ __forceinline__ void rope_cos_sin(int pos, int p, int d_rope, const RopeParams& rp, float& c, float& s) {
+  double theta = pow((double)rp.base, -2.0 * (double)p / (double)d_rope);
+  if (rp.yarn_s > 1.f) {
+    const double r = (double)rp.yarn_orig * theta / (2.0 * M_PI);
+    const double g = fmin(1.0, fmax(0.0, (r - (double)rp.yarn_alpha) / ((double)rp.yarn_beta - (double)rp.yarn_alpha)));
+    theta = (1.0 - g) * theta / (double)rp.yarn_s + g * theta;
+  }
   const double ang = (double)pos * theta;
   double sd, cd;
   sincos(ang, &sd, &cd);
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       c = cs[0];
       s = cs[1];
     } else {
-      rope_cos_sin(pos, p, a.d_rope, (double)a.rope_base, c, s);
+      rope_cos_sin(pos, p, a.d_rope, a.rope, c, s);
     }
     const float x0 = ld_as_f32<TIN>(a.kr, ki + 2 * p), x1 = ld_as_f32<TIN>(a.kr, ki + 2 * p + 1);
     dst[a.d_c + 2 * p] = from_f32<TOUT>(c * x0 - s * x1);
@@ -95,13 +105,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   }
 }
 
-__global__ void rope_table_kernel(float* out, int L, int start_pos, int d_rope, float base) {
+__global__ void rope_table_kernel(float* out, int L, int start_pos, int d_rope, RopeParams rp) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = d_rope / 2;
   if (idx >= (int64_t)L * half) return;
   const int t = (int)(idx / half), p = (int)(idx % half);
   float c, s;
-  rope_cos_sin(start_pos + t, p, d_rope, (double)base, c, s);
+  rope_cos_sin(start_pos + t, p, d_rope, rp, c, s);
   out[idx * 2] = c;
   out[idx * 2 + 1] = s;
 }
@@ -155,10 +165,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, float base, hipStream_t st) {
+hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, const RopeParams& rp,
+                             hipStream_t st) {
   const int64_t n = (int64_t)L * (d_rope / 2);
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, out, L, start_pos, d_rope, base);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, out, L, start_pos, d_rope, rp);
   return hipGetLastError();
 }
 

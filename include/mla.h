@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -86,6 +86,19 @@ typedef struct {
   float rms_eps;       /* RMSNorm epsilon                                  */
   int32_t dtype;       /* mla_dtype                                        */
   int32_t prefill_form; /* mla_prefill_form (mla_prefill only)             */
+  /* YaRN long-context extension (notes page, section 三(二)3: s = 40,
+   * alpha = 1, beta = 32, sqrt(t) = 0.1 ln s + 1, original window 4K; the
+   * method's meaning from the YaRN paper the page points to).  Off when
+   * yarn_s <= 1.  On: every RoPE frequency theta_p (k^R in the cache, q^R in
+   * prefill) becomes (1-g) theta_p / s + g theta_p with g = clamp((r - alpha)
+   * / (beta - alpha), 0, 1), r = yarn_orig_ctx * theta_p / (2 pi), and every
+   * attention logit is multiplied by (0.1 ln s + 1)^2 on top of
+   * softmax_scale (prefill and decode).  mla_decode's q_pe must be rotated
+   * with the same frequencies by the caller. */
+  float yarn_s;
+  float yarn_alpha;
+  float yarn_beta;
+  int32_t yarn_orig_ctx;
 } mla_config;
 
 /* Paged latent cache (host struct holding device pointers).
