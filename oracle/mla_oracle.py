@@ -30,7 +30,10 @@ design notes of the repository):
     [[cos, -sin], [sin, cos]] of section 一(一)3, angle pos * theta_p with
     theta_p = base^(-2p/d_rope) (the RoPE frequency formula quoted on the
     hnwysp.cn digest, section 4.3), base 10000, positions counted from 0.
-  * Output stops at o = [o_1; ...; o_{n_h}]; W^O is not applied.
+  * Output stops at o = [o_1; ...; o_{n_h}]; W^O is applied separately
+    (output_projection), as is its fold with W^UV (【思考】 on absorption:
+    u_t = W^O [o_{t,1}; ...; o_{t,n_h}], W_i^O the d_h-column block of head i,
+    W_i^O' = W_i^O W_i^UV, W^O' = [W_1^O' ... W_{n_h}^O']).
   * YaRN (optional, the long-context extension of the notes page, section
     三(二)3 "长上下文扩展": s = 40, alpha = 1, beta = 32, factor 0.1 ln s + 1,
     with the method's meaning taken from the YaRN paper the page points to):
@@ -213,6 +216,31 @@ def absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, scale: float, heads=
         a = e / e.sum(axis=1, keepdims=True)
         out[:, n] = (a @ c) @ w_uv[i * dh:(i + 1) * dh].T
     return out
+
+
+# ---------------------------------------------------------------------------
+# Output projection (【思考】 on absorption: u_t = W^O [o_{t,1}; ...; o_{t,n_h}])
+# ---------------------------------------------------------------------------
+def output_projection(o, w_o) -> np.ndarray:
+    """u = W^O [o_1; ...; o_{n_h}] for every token: o [T, H, d_h], W^O [d, H*d_h] -> u [T, d]."""
+    o = _f64(o)
+    return o.reshape(o.shape[0], -1) @ _f64(w_o).T
+
+
+def fold_output(w_o, w_uv, n_heads: int) -> np.ndarray:
+    """W^O' = [W_1^O W_1^UV, ..., W_{n_h}^O W_{n_h}^UV]  ([d, H*d_c]).
+
+    W_i^O is the d_h-column block i of W^O; W_i^UV the d_h-row block i of W^UV.
+    """
+    w_o, w_uv = _f64(w_o), _f64(w_uv)
+    dh = w_o.shape[1] // n_heads
+    return np.concatenate([w_o[:, i * dh:(i + 1) * dh] @ w_uv[i * dh:(i + 1) * dh] for i in range(n_heads)], axis=1)
+
+
+def folded_output(o_lat, w_o_fold) -> np.ndarray:
+    """u = W^O' [o^lat_1; ...; o^lat_{n_h}] with o^lat_i = sum_j a_j c_j: o_lat [T, H, d_c] -> u [T, d]."""
+    o_lat = _f64(o_lat)
+    return o_lat.reshape(o_lat.shape[0], -1) @ _f64(w_o_fold).T
 
 
 # ---------------------------------------------------------------------------

@@ -471,3 +471,41 @@ def test_yarn_prefill_s1_equals_plain_prefill():
     b, rb = om.prefill(h, w, s.n_heads, s.rms_eps, s.rope_base, s.scale,
                        yarn=dict(s=1.0, alpha=1.0, beta=32.0, orig_ctx=4096))
     assert _rel(a, b) <= 1e-13 and _rel(ra, rb) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Output projection W^O and its fold with W^UV
+# ---------------------------------------------------------------------------
+def test_wo_fold_equals_unfolded():
+    """The page's equation: W^O [W_1^UV s_1; ...] = W^O' [s_1; ...]."""
+    r = np.random.default_rng(50)
+    T, H, dh, dc, d = 3, 4, 5, 7, 6
+    o_lat = r.standard_normal((T, H, dc))
+    w_uv = r.standard_normal((H * dh, dc))
+    w_o = r.standard_normal((d, H * dh))
+    o = np.stack([o_lat[:, i] @ w_uv[i * dh:(i + 1) * dh].T for i in range(H)], axis=1)
+    a = om.output_projection(o, w_o)
+    b = om.folded_output(o_lat, om.fold_output(w_o, w_uv, H))
+    assert _rel(b, a) <= 1e-13
+    assert om.fold_output(w_o, w_uv, H).shape == (d, H * dc)
+
+
+def test_wo_identity_concatenates_heads():
+    r = np.random.default_rng(51)
+    o = r.standard_normal((2, 3, 4))
+    assert np.array_equal(om.output_projection(o, np.eye(12)), o.reshape(2, 12))
+
+
+def test_wo_head_blocks():
+    """W_i^O is the column block of head i: zeroing every other block leaves
+    only head i's output in u."""
+    r = np.random.default_rng(52)
+    T, H, dh, d = 2, 3, 4, 5
+    o = r.standard_normal((T, H, dh))
+    w_o = r.standard_normal((d, H * dh))
+    for i in range(H):
+        w_i = np.zeros_like(w_o)
+        w_i[:, i * dh:(i + 1) * dh] = w_o[:, i * dh:(i + 1) * dh]
+        o2 = np.zeros_like(o)
+        o2[:, i] = o[:, i]
+        assert np.array_equal(om.output_projection(o, w_i), om.output_projection(o2, w_o))
