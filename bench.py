@@ -174,6 +174,37 @@ def run_prefill_bench(steps: int, warmup: int, form: int, L: int = 8192):
     return dict(wall=wall, attn_ms=attn_ms, flops=prefill_flops(s, L, form == mla.PREFILL_EXPLICIT), L=L)
 
 
+def run_output_projection_bench(steps: int, warmup: int) -> dict:
+    """u = W^O o for the decode workload's 64 rows (W^O: 7168 x 16384 bf16,
+    235 MB), and the folded W^O' (7168 x 65536, 940 MB) on the latent sums
+    instead: the fold removes the W^UV GEMM but reads 4x the weight bytes."""
+    s = mi.V3
+    cfg = mla.Config(**CFG_EXTRA)
+    T = 64
+    res = {"workload": "output projection of one decode step: 64 rows, d=7168, n_h*d_h=16384 (W^O) or "
+                       "n_h*d_c=65536 (folded W^O' = [W_i^O W_i^UV])"}
+    for name, width in (("w_o", s.n_heads * s.d_head), ("folded_w_o", s.n_heads * s.d_c)):
+        x = torch.randn((T, width), device="cuda").bfloat16()
+        w = (torch.randn((s.d_model, width), device="cuda") * width ** -0.5).bfloat16()
+        u = torch.empty((T, s.d_model), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(mla.mla_output_projection_workspace_size(cfg, T, width), 256), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(warmup):
+            mla.mla_output_projection(cfg, x, w, u, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            mla.mla_output_projection(cfg, x, w, u, ws=ws)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / steps * 1e6
+        wbytes = s.d_model * width * 2
+        res[name] = {"us": round(us, 2), "weight_bytes": wbytes, "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, w, u, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The float64 oracle on whole sequences of the decode workload (all 128
     heads, every cached row), one after another until min_seconds have passed."""
@@ -292,6 +323,7 @@ def main():
                      "algorithmic_bytes": d["latent_bytes"],
                      "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
     }
+    res["output_projection"] = run_output_projection_bench(args.steps, args.warmup)
     if not args.no_prefill:
         res["prefill"] = run_prefill_summary(args)
     if not args.no_cpu_baseline:

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "mla_decode_num_splits": (I32, [CP, I32, I32, I32]),
             "mla_decode_profiled": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P, P, P]),
             "mla_prefill_profiled": (I32, [CP, KP, WP, P, I32, I32, I32, P, P, SZ, P, P, P]),
+            "mla_output_projection_workspace_size": (I32, [CP, I32, I32, ctypes.POINTER(SZ)]),
+            "mla_output_projection": (I32, [CP, P, I32, P, P, I32, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -204,6 +206,23 @@ def mla_prefill(cfg: Config, cache: PagedCache, weights: dict, h, out, start_pos
     _check(lib().mla_prefill_profiled(ctypes.byref(cfg._c()), ctypes.byref(cache._c()),
                                       ctypes.byref(_weights(weights)), _ptr(h), B, L, start_pos, _ptr(out), _ptr(ws),
                                       ws.numel(), _stream(stream), ev0, ev1), "mla_prefill")
+
+
+def mla_output_projection_workspace_size(cfg: Config, T: int, width: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mla_output_projection_workspace_size(ctypes.byref(cfg._c()), T, width, ctypes.byref(n)),
+           "mla_output_projection_workspace_size")
+    return n.value
+
+
+def mla_output_projection(cfg: Config, x, w_o, u, ws=None, stream=None) -> None:
+    """u [T, d_model] = x [T, width] W^O^T with W^O [d_model, width] (width = n_heads * d_head,
+    or n_heads * d_c for the folded W^O')."""
+    T, width = x.shape[0], x.numel() // max(x.shape[0], 1)
+    if ws is None:
+        ws = _workspace(max(mla_output_projection_workspace_size(cfg, T, width), 1), x.device)
+    _check(lib().mla_output_projection(ctypes.byref(cfg._c()), _ptr(x), width, _ptr(w_o), _ptr(u), T, _ptr(ws),
+                                       ws.numel(), _stream(stream)), "mla_output_projection")
 
 
 def mla_decode_workspace_size(cfg: Config, B: int, s_q: int, max_kv_len: int) -> int:

@@ -561,4 +561,50 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
   return attend(cfg, bf16, a, DECODE_TARGET_ITEMS, true, true, w_uv, out, st, attn_start, attn_stop);
 }
 
+// Split of the output projection's reduction: enough workgroups to stream W^O
+// at full bandwidth when T is small, each slice at least 512 wide.
+int32_t out_proj_splits(const mla_config* c, bool bf16, int32_t T, int32_t width) {
+  if (!bf16) return 1;
+  const int64_t tiles = ceil_div(T, 128) * ceil_div(c->d_model, 128);
+  int64_t s = ceil_div(768, tiles);
+  s = s < width / 512 ? s : width / 512;
+  while (s > 1 && width % (s * 64) != 0) --s;
+  return s > 1 ? (int32_t)s : 1;
+}
+
+mla_status mla_output_projection_workspace_size(const mla_config* cfg, int32_t T, int32_t width, size_t* bytes) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if (!bytes || T < 0 || width <= 0) return MLA_ERR_INVALID_ARG;
+  const int32_t S = out_proj_splits(cfg, bf16, T, width);
+  *bytes = S > 1 ? (size_t)S * T * cfg->d_model * 4 : 0;
+  return MLA_OK;
+}
+
+mla_status mla_output_projection(const mla_config* cfg, const void* x, int32_t width, const void* w_o, void* u,
+                                 int32_t T, void* ws, size_t ws_bytes, void* stream) {
+  bool bf16;
+  mla_status s = check_cfg(cfg, &bf16);
+  if (s != MLA_OK) return s;
+  if (T < 0 || width <= 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!x || !w_o || !u || !aligned16(x) || !aligned16(w_o) || !aligned16(u)) return MLA_ERR_INVALID_ARG;
+  if (width % 64 != 0 || cfg->d_model % 8 != 0) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)T > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  const int32_t S = out_proj_splits(cfg, bf16, T, width);
+  hipStream_t st = (hipStream_t)stream;
+  const int d = cfg->d_model;
+  if (S == 1)  // u[t, n] = sum_k x[t, k] W^O[n, k]
+    return launch_gemm(bf16, gemm(x, width, 0, w_o, width, 0, u, d, 0, T, d, width, 1, false, bf16), st);
+  if (!ws || !aligned16(ws) || (size_t)S * T * d * 4 > ws_bytes) return MLA_ERR_WORKSPACE;
+  // slice z of the reduction: columns [z*Ks, (z+1)*Ks) of x and W^O into fp32 partial z
+  const int32_t Ks = width / S;
+  if ((s = launch_gemm(true, gemm(x, width, Ks, w_o, width, Ks, ws, d, (int64_t)T * d, T, d, Ks, S, false, false),
+                       st)) != MLA_OK)
+    return s;
+  MLA_HIP(launch_sum_partials((const float*)ws, S, (int64_t)T * d, u, 1, st));
+  return MLA_OK;
+}
+
 }  // extern "C"

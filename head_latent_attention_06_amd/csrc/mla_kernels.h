@@ -113,6 +113,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d_rope, const RopeParams& rp,
                              hipStream_t st);
 
+// out[i] = sum_{z < S} p[z * n + i] (fp32 partials of a split-K GEMM) for
+// i < n, stored in bf16 or fp32; 4 elements per thread (n % 4 == 0).
+hipError_t launch_sum_partials(const float* p, int32_t S, int64_t n, void* out, int32_t bf16_out, hipStream_t st);
+
 // RMSNorm of fp32 rows into the storage dtype: out[r] = x[r] / rms(x[r]) * g.
 hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out, int64_t ldo,
                           int32_t rows, int32_t width, float eps, int32_t bf16_io, hipStream_t st);

@@ -173,6 +173,37 @@ hipError_t launch_rope_table(float* out, int32_t L, int32_t start_pos, int32_t d
   return hipGetLastError();
 }
 
+namespace {
+template <typename TOUT>
+__global__ void sum_partials_kernel(const float* p, int S, int64_t n4, TOUT* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = reinterpret_cast<const float4*>(p)[i];
+  for (int z = 1; z < S; ++z) {
+    const float4 v = reinterpret_cast<const float4*>(p)[(int64_t)z * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  out[4 * i] = from_f32<TOUT>(acc.x);
+  out[4 * i + 1] = from_f32<TOUT>(acc.y);
+  out[4 * i + 2] = from_f32<TOUT>(acc.z);
+  out[4 * i + 3] = from_f32<TOUT>(acc.w);
+}
+}  // namespace
+
+hipError_t launch_sum_partials(const float* p, int32_t S, int64_t n, void* out, int32_t bf16_out, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  if (bf16_out)
+    hipLaunchKernelGGL((sum_partials_kernel<bf16>), dim3(blocks_for(n4, 256)), dim3(256), 0, st, p, S, n4, (bf16*)out);
+  else
+    hipLaunchKernelGGL((sum_partials_kernel<float>), dim3(blocks_for(n4, 256)), dim3(256), 0, st, p, S, n4,
+                       (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out, int64_t ldo, int32_t rows,
                           int32_t width, float eps, int32_t bf16_io, hipStream_t st) {
   if (rows <= 0) return hipSuccess;

@@ -200,6 +200,24 @@ mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const in
                       const void* q_pe, const void* w_uk, const void* w_uv, void* out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Output projection (the absorption passage of the notes page: u_t = W^O
+ * [o_t,1; ...; o_t,n_h], W_i^O the d_h-column block of head i):
+ *   u[t, :] = W^O x[t, :]   for t < T,
+ *  x   [T, width]         the heads' outputs concatenated: mla_prefill's or
+ *                         mla_decode's out viewed as [T, n_heads * d_head]
+ *  w_o [d_model, width]   W^O (width = n_heads * d_head), or the fold
+ *                         W^O' = [W_1^O W_1^UV, ...] of the same passage
+ *                         (width = n_heads * d_c, applied to the latent
+ *                         sums o^lat instead of o)
+ *  u   [T, d_model]
+ * All cfg->dtype; width a multiple of 64, d_model a multiple of 8.  Small T
+ * splits the reduction over width (fp32 partials in the workspace, summed
+ * in a second pass); size the workspace with
+ * mla_output_projection_workspace_size(). */
+mla_status mla_output_projection_workspace_size(const mla_config* cfg, int32_t T, int32_t width, size_t* bytes);
+mla_status mla_output_projection(const mla_config* cfg, const void* x, int32_t width, const void* w_o, void* u,
+                                 int32_t T, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement variants: identical to mla_decode / mla_prefill, and in
  * addition record attn_start and attn_stop (hipEvent_t, either may be NULL) on
  * `stream` immediately before and after the latent-attention kernel, so a

@@ -131,3 +131,17 @@ def test_prefill_form_selection(lib):
     assert _prefill_ws(lib, 1, 64, 0, **kw)[0] == mla.MLA_OK
     assert _prefill_ws(lib, 1, 64, 0, prefill_form=mla.PREFILL_EXPLICIT, **kw)[0] == mla.MLA_ERR_UNSUPPORTED
     assert _prefill_ws(lib, 1, 64, 0, prefill_form=7)[0] == mla.MLA_ERR_INVALID_ARG
+
+
+def test_output_projection_workspace(lib):
+    n = ctypes.c_size_t()
+    # decode-sized T splits the 16384-wide reduction (fp32 partials)
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(_cfg()), 64, 128 * 128, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value >= 2 * 64 * 7168 * 4
+    # prefill-sized T runs one GEMM straight into u
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(_cfg()), 8192, 128 * 128, ctypes.byref(n)) == mla.MLA_OK
+    assert n.value == 0
+    assert lib.mla_output_projection_workspace_size(ctypes.byref(_cfg()), 64, 0, ctypes.byref(n)) == mla.MLA_ERR_INVALID_ARG
+    # a call with a misaligned pointer is refused before any launch
+    assert lib.mla_output_projection(ctypes.byref(_cfg()), FAKE + 2, 16384, FAKE, FAKE, 64, FAKE, 1 << 30,
+                                     None) == mla.MLA_ERR_INVALID_ARG
