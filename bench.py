@@ -239,11 +239,11 @@ def run_prefill_summary(args) -> dict:
     """Both attention forms on the same workload; the explicit form (what
     mla_prefill picks by itself here) is the main entry, the absorbed form is
     reported beside it."""
-    steps = max(2, args.steps // 4)
+    steps = max(2, min(args.steps // 4, 10))  # prefill steps are milliseconds long
     res = {"workload": "MLA causal prefill, B=1, L=8192, d=7168, all projections + append + attention"}
     for form, name, kernel in ((mla.PREFILL_EXPLICIT, "explicit", "fa_bf16_kernel"),
                                (mla.PREFILL_ABSORBED, "absorbed", "attn_bf16_kernel")):
-        p = run_prefill_bench(steps, max(1, args.warmup // 2), form)
+        p = run_prefill_bench(steps, max(2, min(args.warmup // 2, 10)), form)
         pms = p["wall"] / steps * 1e3
         f = p["flops"]
         achieved = f["attention"] / (p["attn_ms"] * 1e-3) / 1e12
@@ -279,8 +279,11 @@ def measured_traffic(path: str = os.path.join(ROOT, "profiles", "attn_bf16_decod
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # From idle the GPU needs ~50 ms of sustained load to reach its steady
+    # clock: decode steps after 20 warm-up steps take ~130 us, after 500 (or
+    # 2000) ~110 us.  500 decode steps are ~60 ms.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill workload (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

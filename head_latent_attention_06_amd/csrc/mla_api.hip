@@ -16,6 +16,7 @@ constexpr int ATTN_SPLIT_PAGES = 1536;  // page ids one attention workgroup stag
 constexpr int DECODE_TARGET_ITEMS = 256;  // about one workgroup per CU for even batches
 constexpr int RAGGED_FACTOR = 4;          // the plan uses 4x as many chunks for ragged ones
 constexpr int MIN_CHUNK = 256;
+constexpr int MERGE_WUV_MAX_ROWS = 256;   // above this the merge and a W^UV GEMM run separately
 
 struct Carve {
   unsigned char* base;
@@ -302,6 +303,11 @@ mla_status attend(const mla_config* c, bool bf16, const AttnArgs& a, int32_t tar
     if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));
     MLA_HIP(launch_attn_bf16(a, st));
     if (ev1) MLA_HIP(hipEventRecord((hipEvent_t)ev1, st));
+    if (need_merge && rows <= MERGE_WUV_MAX_ROWS && c->d_head == 128) {
+      // merge and W^UV in one pass
+      MLA_HIP(launch_merge_wuv_bf16(a, w_uv, out, st));
+      return MLA_OK;
+    }
     if (need_merge) MLA_HIP(launch_merge_bf16(a, st));
   } else {
     if (ev0) MLA_HIP(hipEventRecord((hipEvent_t)ev0, st));

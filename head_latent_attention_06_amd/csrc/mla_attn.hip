@@ -613,6 +613,132 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(AttnArgs a) {
   *reinterpret_cast<u32x4*>((bf16*)a.o_lat + (row * a.H + head) * DC + 8 * t) = outv;
 }
 
+// Merge of the split partials fused with o = W_i^UV o_lat (a6 and a7 in one
+// pass, for up to a few hundred query rows).  Workgroup = (head, 32 query
+// rows), 4 waves.  Phase 1: the 32 rows' o_lat (one chunk: the attention
+// kernel's o_lat; several: the merge above, in registers) go to LDS as bf16.
+// Phase 2: out[r, head, n] = sum_k o_lat[r, k] W^UV[head*128 + n, k] on the
+// MFMA, wave w taking n = 32w .. 32w+31; W^UV's rows are loaded straight into
+// B-operand registers at the start, so they arrive during phase 1.
+constexpr int MW_ROWS = 32, MW_RS = DC * 2 + 16;  // rows per workgroup; LDS row stride (bytes)
+constexpr int MW_BATCH = 4;                       // split partials per row loaded together
+__global__ __launch_bounds__(256) void merge_wuv_bf16_kernel(AttnArgs a, const bf16* __restrict__ w_uv,
+                                                             bf16* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char ot[MW_ROWS * MW_RS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int H = a.H, head = (int)(blockIdx.x % H);
+  const int r0 = (int)(blockIdx.x / H) * MW_ROWS;
+  const int n_rows = a.B * a.s_q;
+  // B operand of step s: W^UV row head*128 + 32 wave + l32, columns 16 s + 8 hi .. + 7
+  const bf16* wrow = w_uv + ((int64_t)head * 128 + 32 * wave + l32) * DC + 8 * hi;
+  u32x4 bw[DC / 16];
+#pragma unroll
+  for (int s = 0; s < DC / 16; ++s) bw[s] = ld16(wrow + 16 * s);
+
+  // phase 1: thread handles 16-byte chunk `lane` of rows wave + 4 i, i < 8.
+  // The loads of all eight rows (up to MW_BATCH partials each) are issued
+  // before any is used; a row with more partials finishes in a loop.
+  constexpr int NR = MW_ROWS / 4;
+  const int32_t* row_off = a.plan + 2;
+  int i0[NR], n[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + wave + 4 * i;
+    i0[i] = r < n_rows ? row_off[r] : 0;
+    n[i] = r < n_rows ? row_off[r + 1] - i0[i] : 0;
+  }
+  u32x4 v[NR][MW_BATCH];
+  float mk[NR][MW_BATCH], lk[NR][MW_BATCH];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + wave + 4 * i;
+#pragma unroll
+    for (int k = 0; k < MW_BATCH; ++k) {
+      mk[i][k] = -INFINITY;
+      lk[i][k] = 0.f;
+      v[i][k] = u32x4{0u, 0u, 0u, 0u};
+      if (n[i] == 1 && k == 0) {  // one chunk: the attention kernel wrote o_lat itself
+        mk[i][0] = 0.f;
+        lk[i][0] = 1.f;
+        v[i][0] = ld16((const bf16*)a.o_lat + ((int64_t)r * H + head) * DC + 8 * lane);
+      } else if (n[i] > 1 && k < n[i]) {
+        const int64_t slot = (int64_t)(i0[i] + k) * H + head;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+        mk[i][k] = ml.x;
+        lk[i][k] = ml.y;
+        v[i][k] = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float mstar = -INFINITY, L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // o = sum_k 2^(m_k - m*) l_k o_k / sum_k 2^(m_k - m*) l_k over batches of partials
+    auto add_batch = [&](const u32x4 (&vb)[MW_BATCH], const float (&mb_)[MW_BATCH], const float (&lb)[MW_BATCH]) {
+      float mb = mstar;
+#pragma unroll
+      for (int k = 0; k < MW_BATCH; ++k) mb = fmaxf(mb, mb_[k]);
+      if (mb == -INFINITY) return;
+      const float alpha = exp2f(mstar - mb);
+      L *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+      mstar = mb;
+#pragma unroll
+      for (int k = 0; k < MW_BATCH; ++k) {
+        const float wk = lb[k] > 0.f ? exp2f(mb_[k] - mstar) * lb[k] : 0.f;
+        L += wk;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] += wk * bf16_lo(vb[k][d]);
+          acc[2 * d + 1] += wk * bf16_hi(vb[k][d]);
+        }
+      }
+    };
+    add_batch(v[i], mk[i], lk[i]);
+    for (int k0 = MW_BATCH; k0 < n[i]; k0 += MW_BATCH) {  // rows with more partials
+      u32x4 vb[MW_BATCH];
+      float mb_[MW_BATCH], lb[MW_BATCH];
+#pragma unroll
+      for (int k = 0; k < MW_BATCH; ++k) {
+        mb_[k] = -INFINITY;
+        lb[k] = 0.f;
+        vb[k] = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + k < n[i]) {
+          const int64_t slot = (int64_t)(i0[i] + k0 + k) * H + head;
+          const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+          mb_[k] = ml.x;
+          lb[k] = ml.y;
+          vb[k] = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
+        }
+      }
+      add_batch(vb, mb_, lb);
+    }
+    u32x4 res = {0u, 0u, 0u, 0u};
+    if (L > 0.f) {
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) res[d] = pack_bf16x2(acc[2 * d] * inv, acc[2 * d + 1] * inv);
+    }
+    *reinterpret_cast<u32x4*>(ot + (wave + 4 * i) * MW_RS + 16 * lane) = res;
+  }
+  __syncthreads();
+
+  // phase 2: D[row][n] over the 32 rows and this wave's 32 columns
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DC / 16; ++s)
+    acc = mfma32(*reinterpret_cast<const u32x4*>(ot + l32 * MW_RS + (2 * s + hi) * 16), bw[s], acc);
+  // lane (l32, hi), register 4 g + e: row 8 g + 4 hi + e, column 32 wave + l32
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+    if (r < n_rows) out[((int64_t)r * H + head) * 128 + 32 * wave + l32] = (bf16)acc[i];
+  }
+}
+
 // Work plan: one workgroup of 256 threads (wave-level scans, three barriers
 // per 256 rows).
 __global__ __launch_bounds__(256) void plan_kernel(AttnArgs a, int32_t* plan, int32_t target_items,
@@ -716,6 +842,13 @@ hipError_t launch_merge_bf16(const AttnArgs& a, hipStream_t st) {
   const int64_t n = (int64_t)a.B * a.s_q * (a.H / 4);  // H is a multiple of 32 on this path
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_wuv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t st) {
+  const int64_t n = (int64_t)a.H * ((a.B * a.s_q + MW_ROWS - 1) / MW_ROWS);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_wuv_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a, (const bf16*)w_uv, (bf16*)out);
   return hipGetLastError();
 }
 

@@ -50,6 +50,9 @@ hipError_t launch_attn_plan(const AttnArgs& a, int32_t* plan, int32_t target_ite
                             int32_t max_chunk, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge_bf16(const AttnArgs& a, hipStream_t st);
+// merge (as launch_merge_bf16) fused with out[r, i, :] = W_i^UV o_lat[r, i, :]
+// (d_head = 128); w_uv [H*128, 512], out [n_rows, H, 128] bf16
+hipError_t launch_merge_wuv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 
 // Batched GEMM C[z][m][n] = sum_k A[z][m][k] * B[z](k, n) with fp32 accumulation.
