@@ -205,6 +205,52 @@ def run_output_projection_bench(steps: int, warmup: int) -> dict:
     return res
 
 
+def run_other_decode(steps: int, warmup: int) -> dict:
+    """The long-context (B=4 x 131072) and ragged (B=128, context ~ U{1..32768},
+    s_q=2) decode workloads.  Cache, queries and weights are drawn on the device
+    (seeded torch generator, N(0,1), W ~ N(0, 1/d_c)); lengths and the
+    shuffled block tables come from mla_inputs."""
+    s = mi.V3
+    cfg = mla.Config(**CFG_EXTRA)
+    res = {}
+    for cid, name, s_q in ((4, "long_context_b4_131072", 1), (5, "ragged_b128_u1_32768_sq2", 2)):
+        ctx = mi.config_context_lens(cid)
+        kv = (ctx + s_q).astype(np.int32)
+        B, max_kv = len(kv), int(kv.max())
+        bt, npages = mi.block_table(cid, kv, s.page_size, shuffle=True)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cid)
+        pool = torch.randn((npages, s.page_size, cfg.row), generator=g, device="cuda").bfloat16()
+        cache = mla.PagedCache(pool, torch.from_numpy(bt).cuda())
+        q_nope = torch.randn((B, s_q, s.n_heads, s.d_head), generator=g, device="cuda").bfloat16()
+        q_pe = torch.randn((B, s_q, s.n_heads, s.d_rope), generator=g, device="cuda").bfloat16()
+        w_uk = (torch.randn((s.n_heads * s.d_head, s.d_c), generator=g, device="cuda") * s.d_c ** -0.5).bfloat16()
+        w_uv = (torch.randn((s.n_heads * s.d_head, s.d_c), generator=g, device="cuda") * s.d_c ** -0.5).bfloat16()
+        kvd = torch.from_numpy(kv).cuda()
+        out = torch.empty((B, s_q, s.n_heads, s.d_head), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mla.mla_decode_workspace_size(cfg, B, s_q, max_kv), dtype=torch.uint8, device="cuda")
+        for _ in range(warmup):
+            mla.mla_decode(cfg, cache, kvd, max_kv, q_nope, q_pe, w_uk, w_uv, out, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            mla.mla_decode(cfg, cache, kvd, max_kv, q_nope, q_pe, w_uk, w_uv, out, ws=ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        nbytes = int(kv.sum()) * cfg.row * 2
+        # keys each query sees (causal within the s_q new tokens)
+        pairs = int(sum(int(k) - s_q + i + 1 for k in kv for i in range(s_q)))
+        flops = pairs * s.n_heads * (cfg.row + cfg.d_c) * 2
+        res[name] = {"ms_per_step": round(ms, 4), "latent_bytes": nbytes,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pool, cache, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The float64 oracle on whole sequences of the decode workload (all 128
     heads, every cached row), one after another until min_seconds have passed."""
@@ -288,6 +334,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill workload (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--other-decode", action="store_true",
+                    help="also time the long-context and ragged decode workloads (not in the default run)")
     ap.add_argument("--yarn", action="store_true",
                     help="run both workloads with the YaRN long-context settings (s=40, alpha=1, beta=32, 4K window)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -327,6 +375,8 @@ def main():
                      "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
     }
     res["output_projection"] = run_output_projection_bench(args.steps, args.warmup)
+    if args.other_decode:
+        res["other_decode"] = run_other_decode(max(10, args.steps // 4), max(20, args.warmup // 4))
     if not args.no_prefill:
         res["prefill"] = run_prefill_summary(args)
     if not args.no_cpu_baseline:
