@@ -133,3 +133,27 @@ def test_prefill_bf16_chunked_matches_whole(form):
     ref, _ = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=np.arange(96, 160))
     assert rel_l2(host(out_tail)[0], ref) <= BF16_TOL
     assert rel_l2(host(out_tail)[0], host(out_all)[0, 96:]) <= 5e-3
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_bf16_two_sequences_after_prefix(form):
+    """B=2, 200 cached tokens, then 300 new ones (two 256-query groups, the
+    diagonal off every tile boundary); checked on sampled tokens."""
+    s = mi.V3
+    w = mi.weights(35, s)
+    h = mi.hidden(35, s, 2, 500)
+    bt, npages = mi.block_table(36, [500, 500], s.page_size, shuffle=True)
+    cfg = config(s, torch.bfloat16)
+    cfg.prefill_form = form
+    cache = paged_cache(cfg, npages, bt)
+    _prefill(s, torch.bfloat16, 35, 2, 200, w=w, h=h[:, :200], cache=cache, form=form)
+    _, _, _, _, out = _prefill(s, torch.bfloat16, 35, 2, 300, start_pos=200, w=w, h=h[:, 200:], cache=cache,
+                               form=form)
+    toks = np.array([0, 1, 55, 56, 255, 256, 299])
+    for b in range(2):
+        ref, _ = om.prefill(h[b], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=200 + toks,
+                            heads=[0, 64, 127])
+        err = rel_l2(host(out)[b][toks][:, [0, 64, 127]], ref)
+        print(f"b={b} rel_l2={err:.3e}")
+        assert err <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
