@@ -17,6 +17,9 @@
 // in registers while staging.  Ragged M and N are handled by buffer-resource
 // bounds (out-of-range rows load as zero) and masked stores; K must be a
 // multiple of 64.
+#include <algorithm>
+#include <utility>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_plan.h"
@@ -193,6 +196,251 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     }
 }
 
+// ---- large-tile GEMM (B given [N, K]) ---------------------------------------
+// Output tile 256 x BN (BN = 256 or 192), four waves in a 2 x 2 arrangement,
+// each wave a 128 x BN/2 block of 32 x 32 accumulators in AGPRs, so every
+// 16-byte LDS fragment read feeds BN/64 or 4 MFMAs.  K moves in slices of 32
+// through a ring of four LDS stages filled by direct-to-LDS buffer loads (three
+// slices in flight).  Each 64-byte tile row keeps its four 16-byte chunks at
+// chunk ^ ((row >> 1) & 3), which keeps the fragment reads free of bank
+// conflicts; the loads apply the permutation on the global side.  The
+// product is formed transposed (C^T = B A^T) so each lane holds four
+// consecutive output columns and stores them with one vector store.
+constexpr int GB_BM = 256, GB_BK = 32, GB_NST = 4, GB_GM = 4;
+constexpr int GB_ROW = GB_BK * 2;  // bytes per tile row
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds_addr + 16 * lane
+__device__ __forceinline__ void gb_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int32_t voff, int32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void gb_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ u32x4 gb_lds16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)addr;
+}
+template <typename T>
+__device__ __forceinline__ const T* gb_uniform(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int BN, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_big_kernel(GemmArgs g) {
+  constexpr int A_BYTES = GB_BM * GB_ROW, B_BYTES = BN * GB_ROW, STG = A_BYTES + B_BYTES;
+  constexpr int TN = BN / 64;                  // 32-column tuples per wave (4 or 3)
+  constexpr int NA = GB_BM / 16 / 4;           // A loads per wave per slice (4)
+  constexpr int NB = BN / 16 / 4;              // B loads per wave per slice (4 or 3)
+  constexpr int NLD = NA + NB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[GB_NST * STG];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Tile order: consecutive ids run on one XCD (xcd_remap); within a group of
+  // GB_GM row tiles the column tile advances every GB_GM ids, so the ~32
+  // workgroups an XCD runs at once cover about 4 x 8 tiles and share their
+  // A and B slices in that XCD's L2.
+  const int tiles_n = (g.N + BN - 1) / BN, tiles_m = (g.M + GB_BM - 1) / GB_BM;
+  const int r = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int group = r / (GB_GM * tiles_n), first_m = group * GB_GM;
+  const int gsz = min(GB_GM, tiles_m - first_m), idx = r - group * GB_GM * tiles_n;
+  const int tm = first_m + idx % gsz, tn = idx / gsz;
+  const int z = blockIdx.y;
+  const int m0 = tm * GB_BM, n0 = tn * BN;
+  const unsigned char* A = (const unsigned char*)g.A + (int64_t)z * g.strideA * 2;
+  const unsigned char* B = (const unsigned char*)g.B + (int64_t)z * g.strideB * 2;
+  const int64_t lda2 = g.lda * 2, ldb2 = g.ldb * 2;
+
+  // Load i of wave w moves tile rows 16 (4 i + w) .. +15 (64 bytes each):
+  // lane l writes LDS bytes 16 l of that 1 KB, i.e. row + l/4, slot l%4,
+  // holding the row's logical chunk (l%4) ^ ((l/8) & 3).
+  const int32_t va = (int32_t)((lane >> 2) * lda2) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+  const int32_t vb = (int32_t)((lane >> 2) * ldb2) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  const int nk = g.K / GB_BK;
+  // One buffer resource per load, built once: rows past M (or N) lie outside
+  // it and load as zero; the slice's k offset goes in the scalar offset.
+  __amdgpu_buffer_rsrc_t rsa[NA], rsb[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = 16 * (4 * i + wave);
+    const int rows = max(0, min(16, g.M - m0 - row));
+    const int32_t nbytes = rows > 0 ? (int32_t)((rows - 1) * lda2 + g.K * 2) : 0;
+    rsa[i] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(gb_uniform(A + (int64_t)(m0 + row) * lda2)), (short)0, nbytes, 0x00020000);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + 16 * (4 * i + wave);  // first weight row of this load
+    const unsigned char* p;
+    int rows;
+    if (g.B2 && n >= g.n_split) {
+      p = (const unsigned char*)g.B2 + (int64_t)(n - g.n_split) * ldb2;
+      rows = min(16, g.N - n);
+    } else {
+      p = B + (int64_t)n * ldb2;
+      rows = min(16, (g.B2 ? g.n_split : g.N) - n);
+    }
+    const int32_t nbytes = rows > 0 ? (int32_t)((rows - 1) * ldb2 + g.K * 2) : 0;
+    rsb[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(gb_uniform(p)), (short)0, nbytes,
+                                               0x00020000);
+  }
+  // slice kt (past the end: the last slice again, into a stage nobody reads,
+  // so every slice issues the same loads and the vmcnt bookkeeping stays uniform)
+  // load n (< NA: A rows, else B rows) of slice kt
+  auto issue_one = [&](int kt, int n) {
+    const int32_t kb = __builtin_amdgcn_readfirstlane(min(kt, nk - 1) * GB_BK * 2);
+    const uint32_t st = sbase + (kt % GB_NST) * STG;
+    if (n < NA)
+      gb_dma16(rsa[n], st + 16 * (4 * n + wave) * GB_ROW, va, kb);
+    else
+      gb_dma16(rsb[n - NA], st + A_BYTES + 16 * (4 * (n - NA) + wave) * GB_ROW, vb, kb);
+  };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) issue_one(kt, n);
+  };
+
+  // Fragment of tile row R (lane l32), k step ks: bytes R*64 + 16 ((2 ks + hi) ^ ((R >> 1) & 3))
+  // = (R*64 + 16 (hi ^ ((R >> 1) & 3))) ^ 32 ks.
+  const int ra = wm * 128 + l32, rb = wn * (BN / 2) + l32;
+  const uint32_t fa = ra * GB_ROW + 16 * (hi ^ ((ra >> 1) & 3));            // + 32 mi rows: same XOR term
+  const uint32_t fb = A_BYTES + rb * GB_ROW + 16 * (hi ^ ((rb >> 1) & 3));  // + 32 ni rows likewise
+  u32x4 af[2][4], bfr[2][TN];
+  auto load_frags = [&](int set, int kt, int ks) {
+    const uint32_t st = sbase + (kt % GB_NST) * STG;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[set][i] = gb_lds16((st + fa + i * 32 * GB_ROW) ^ (32 * ks));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[set][j] = gb_lds16((st + fb + j * 32 * GB_ROW) ^ (32 * ks));
+  };
+
+  f32x16 acc[4][TN];  // [m tuple][n tuple], C^T layout
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  issue(0);
+  issue(1);
+  issue(2);
+  gb_wait_vmcnt<2 * NLD>();
+  __syncthreads();
+  load_frags(0, 0, 0);
+  // k step of one slice: 4 x TN MFMAs on fragment set `set`, interleaved with
+  // the loads of the other set
+  auto kstep = [&](int set, auto&& loads) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+            : "+a"(acc[i][j])
+            : "v"(bfr[set][j]), "v"(af[set][i]));
+        loads(i, j);
+        __builtin_amdgcn_sched_barrier(0);  // keep the MFMA / load interleave as written
+      }
+  };
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t st = sbase + (kt % GB_NST) * STG;
+    // k step 0, reading k step 1's fragments
+    kstep(0, [&](int i, int j) {
+      if (j != 0) return;
+      af[1][i] = gb_lds16((st + fa + i * 32 * GB_ROW) ^ 32);
+      if (i < TN) bfr[1][i] = gb_lds16((st + fb + i * 32 * GB_ROW) ^ 32);
+    });
+    // slice kt+1 has landed everywhere and every wave is done with slice kt-1's stage
+    gb_wait_vmcnt<NLD>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 1, reading the next slice's k step 0; slice kt+3's loads are
+    // spread over its MFMAs (a burst would hold up the MFMA issue)
+    const uint32_t sn = sbase + ((kt + 1) % GB_NST) * STG;
+    kstep(1, [&](int i, int j) {
+      if (j == 0) {
+        af[0][i] = gb_lds16(sn + fa + i * 32 * GB_ROW);
+        if (i < TN) bfr[0][i] = gb_lds16(sn + fb + i * 32 * GB_ROW);
+      }
+      const int m = i * TN + j;  // load n goes out after MFMA n * 4 TN / NLD
+#pragma unroll
+      for (int n = 0; n < NLD; ++n)
+        if (n * 4 * TN / NLD == m) issue_one(kt + 3, n);
+    });
+  }
+  gb_wait_vmcnt<0>();  // the empty slices' loads still write LDS
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // Output through LDS, one wave's 128 x BN/2 block at a time per wave-private
+  // quarter of the stage memory, so every store instruction writes whole rows: lane (l32, hi)
+  // of acc[i][j] holds row 32 i + l32, columns 32 j + 8 q + 4 hi .. +3 (register
+  // 4 q + e).  The block goes through in passes of PR rows; 16-byte chunk c of
+  // a staged row sits at c ^ (row % CPR) (CPR chunks per row), which keeps the
+  // writes (one row per lane) and the row-contiguous reads free of conflicts;
+  // rows of 12 or 24 chunks (192 columns) rotate by the row instead.
+  __syncthreads();  // every wave is done with the k-slice stages
+  constexpr int ES = OUT_BF16 ? 2 : 4;                 // output element bytes
+  constexpr int RB = (BN / 2) * ES;                    // staged row bytes (256 / 192 or 512 / 384)
+  constexpr int CPR = RB / 16;                         // chunks per row
+  constexpr int PR = 32768 / RB >= 128 ? 128 : 64;     // rows per pass (whole 32-row tuples)
+  constexpr bool POW2 = (CPR & (CPR - 1)) == 0;
+  // staged position of chunk c of row r, and its inverse
+  const auto perm = [](int c, int r) { return POW2 ? c ^ (r & (CPR - 1)) : (c + r) % CPR; };
+  const auto iperm = [](int p, int r) { return POW2 ? p ^ (r & (CPR - 1)) : (p + CPR - r % CPR) % CPR; };
+  constexpr int EREG = GB_NST * STG / 4;  // each wave's share of the stage memory
+  static_assert(PR * RB <= EREG, "staging pass exceeds the wave's LDS share");
+  const uint32_t ew = sbase + wave * EREG;
+  const int col0 = n0 + (BN / 2) * wn;
+  unsigned char* cbase = (unsigned char*)g.C + (int64_t)z * g.strideC * ES;
+#pragma unroll
+  for (int pass = 0; pass < 128 / PR; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < PR / 32; ++ii) {
+      const int i = pass * (PR / 32) + ii;
+      const int r = 32 * ii + l32;  // row within the pass
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& t = acc[i][j];
+          const int c = (32 * j + 8 * q + 4 * hi) * ES;  // byte column within the row
+          if (OUT_BF16) {
+            const u32x2 v = {pack_bf16x2(t[4 * q], t[4 * q + 1]), pack_bf16x2(t[4 * q + 2], t[4 * q + 3])};
+            const uint32_t addr = ew + r * RB + (perm(c >> 4, r) << 4) + (c & 15);
+            *(__attribute__((address_space(3))) u32x2*)addr = v;
+          } else {
+            const f32x4 v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+            const uint32_t addr = ew + r * RB + (perm(c >> 4, r) << 4);
+            *(__attribute__((address_space(3))) f32x4*)addr = v;
+          }
+        }
+    }
+    // (a wave reads back only its own writes: LDS ops of one wave complete in order)
+    // lane l reads chunk position l % CPR of staged row l / CPR (+ 64 / CPR per
+    // step; with 12 or 24 chunks per row the last 4 or 16 lanes idle)
+    constexpr int RSTEP = 64 / CPR;  // rows per read instruction
+#pragma unroll 4
+    for (int rr = 0; rr < PR; rr += RSTEP) {
+      const int r = rr + lane / CPR, pos = lane % CPR;
+      if (lane >= CPR * RSTEP || r >= PR) continue;
+      const u32x4 v = gb_lds16(ew + r * RB + pos * 16);
+      const int row = m0 + 128 * wm + pass * PR + r;
+      const int col = col0 + (iperm(pos, r) * 16) / ES;
+      if (row < g.M && col < g.N) *reinterpret_cast<u32x4*>(cbase + ((int64_t)row * g.ldc + col) * ES) = v;
+    }
+  }
+}
+
 // fp32 SIMT GEMM for small shapes: 16 x 16 output tile per 256 threads.
 template <bool B_KN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
@@ -367,11 +615,50 @@ void launch_smallm(const GemmArgs& g, const PlanJob& pj, hipStream_t st) {
 }
 }  // namespace
 
+namespace {
+// The large-tile kernel: B given [N, K], 16-byte aligned rows, K a multiple of
+// 32, whole 4-column output groups, and enough rows to fill its 256-row tiles.
+bool bigtile_form(const GemmArgs& g) {
+  const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const int cw = g.out_bf16 ? 8 : 4;  // output elements per 16-byte store
+  return !g.b_kn && g.M >= GB_BM && g.K % GB_BK == 0 && g.N % cw == 0 && g.ldc % cw == 0 && g.lda % 8 == 0 &&
+         g.ldb % 8 == 0 && g.strideA % 8 == 0 && g.strideB % 8 == 0 && g.strideC % cw == 0 && al16(g.A) &&
+         al16(g.B) && al16(g.C) && (!g.B2 || (al16(g.B2) && g.n_split % 16 == 0)) &&
+         (int64_t)15 * g.lda * 2 + g.K * 2 < (1LL << 31) && (int64_t)15 * g.ldb * 2 + g.K * 2 < (1LL << 31);
+}
+template <int BN>
+void launch_big(const GemmArgs& g, hipStream_t st) {
+  const unsigned tiles = (unsigned)(((g.M + GB_BM - 1) / GB_BM) * ((g.N + BN - 1) / BN));
+  dim3 grid(tiles, (unsigned)g.batch);
+  if (g.out_bf16)
+    hipLaunchKernelGGL((gemm_big_kernel<BN, true>), grid, dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<BN, false>), grid, dim3(256), 0, st, g);
+}
+}  // namespace
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (smallm_form(g)) {
     launch_smallm<false>(g, PlanJob{}, st);
     return hipGetLastError();
+  }
+  if (bigtile_form(g)) {
+    // the column tile (256 or 192) that keeps more CUs busy over the launch's
+    // rounds of 256 workgroups; too few tiles for either: the 128 x 128 kernel
+    const auto fill = [&](int bn) {
+      const int64_t t = (int64_t)((g.M + GB_BM - 1) / GB_BM) * ((g.N + bn - 1) / bn) * g.batch;
+      const double useful = (double)g.M * g.N * g.batch / ((double)t * GB_BM * bn);
+      return std::make_pair(t, useful * (double)t / (double)(((t + 255) / 256) * 256));
+    };
+    const auto f256 = fill(256), f192 = fill(192);
+    if (std::max(f256.first, f192.first) >= 128) {
+      if (f192.second > f256.second + 0.02)
+        launch_big<192>(g, st);
+      else
+        launch_big<256>(g, st);
+      return hipGetLastError();
+    }
   }
   const unsigned tiles = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles, (unsigned)g.batch);
