@@ -324,10 +324,11 @@ mla_status attend(const mla_config* c, bool bf16, const AttnArgs& a, int32_t tar
 // workspace: RoPE of q^R, k^C = W^UK c and v^C = W^UV c for rows
 // [0, start_pos + L) of every sequence, then causal attention.
 mla_status prefill_explicit(const mla_config* c, const mla_kv_cache* k, const mla_weights* w, int32_t B, int32_t L,
-                            int32_t start_pos, const PrefillWs& p, void* out, hipStream_t st, void* ev0, void* ev1) {
+                            int32_t start_pos, const PrefillWs& p, bool qr_done, void* out, hipStream_t st, void* ev0,
+                            void* ev1) {
   const int T = B * L, H = c->n_heads, row = c->d_c + c->d_rope, kv_end = start_pos + L;
   const int nk = B * kv_end;
-  MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.qr, c->d_rope, 0, T, H, c->d_rope, 1, st));
+  if (!qr_done) MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.qr, c->d_rope, 0, T, H, c->d_rope, 1, st));
   GatherArgs g{};
   g.pool = k->pool; g.num_pages = k->num_pages;
   g.block_table = k->block_table; g.max_pages = k->max_pages_per_seq; g.page_size = c->page_size;
@@ -483,11 +484,26 @@ mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache
   if ((s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_uq, cfg->d_cq, 0, p.qc, (int64_t)H * cfg->d_head, 0, T,
                                   H * cfg->d_head, cfg->d_cq, 1, false, bf16), st)) != MLA_OK)
     return s;
-  // step (3): q^R = RoPE(W^QR c^Q), written next to the absorbed query
-  if ((s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_qr, cfg->d_cq, 0, p.qr_raw, (int64_t)H * cfg->d_rope, 0,
-                                  T, H * cfg->d_rope, cfg->d_cq, 1, false, false), st)) != MLA_OK)
+  // step (3): q^R = RoPE(W^QR c^Q).  Explicit form: the rotation runs in the
+  // GEMM's output stage where that form applies; otherwise the GEMM writes fp32
+  // and a separate pass rotates (into the absorbed query for that form).
+  bool qr_done = false;
+  if (p.use_explicit) {
+    GemmArgs gq = gemm(p.cq, cfg->d_cq, 0, w->w_qr, cfg->d_cq, 0, p.qr, (int64_t)H * cfg->d_rope, 0, T,
+                       H * cfg->d_rope, cfg->d_cq, 1, false, true);
+    gq.rope_cs = p.rope_cs; gq.rope_rows = L; gq.rope_d = cfg->d_rope;
+    const hipError_t e = launch_gemm_bf16_rope(gq, st);
+    if (e == hipSuccess)
+      qr_done = true;
+    else if (e != hipErrorNotSupported)
+      return MLA_ERR_HIP;
+  }
+  if (!qr_done && (s = launch_gemm(bf16, gemm(p.cq, cfg->d_cq, 0, w->w_qr, cfg->d_cq, 0, p.qr_raw,
+                                              (int64_t)H * cfg->d_rope, 0, T, H * cfg->d_rope, cfg->d_cq, 1, false,
+                                              false), st)) != MLA_OK)
     return s;
-  if (p.use_explicit) return prefill_explicit(cfg, cache, w, B, L, start_pos, p, out, st, attn_start, attn_stop);
+  if (p.use_explicit)
+    return prefill_explicit(cfg, cache, w, B, L, start_pos, p, qr_done, out, st, attn_start, attn_stop);
   MLA_HIP(launch_rope_heads(p.qr_raw, p.rope_cs, L, p.q_abs, row, cfg->d_c, T, H, cfg->d_rope, bf16, st));
   // absorption: q_lat_i = W_i^UK^T q^C_i  (batched over heads, W_i^UK given [d_h, d_c])
   if ((s = launch_gemm(bf16, gemm(p.qc, (int64_t)H * cfg->d_head, cfg->d_head, w->w_uk, cfg->d_c,

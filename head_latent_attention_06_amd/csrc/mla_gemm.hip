@@ -231,7 +231,7 @@ __device__ __forceinline__ const T* gb_uniform(const T* p) {
   return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int BN, bool OUT_BF16>
+template <int BN, bool OUT_BF16, bool ROPE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_big_kernel(GemmArgs g) {
   constexpr int A_BYTES = GB_BM * GB_ROW, B_BYTES = BN * GB_ROW, STG = A_BYTES + B_BYTES;
@@ -415,7 +415,18 @@ void gemm_big_kernel(GemmArgs g) {
           const f32x16& t = acc[i][j];
           const int c = (32 * j + 8 * q + 4 * hi) * ES;  // byte column within the row
           if (OUT_BF16) {
-            const u32x2 v = {pack_bf16x2(t[4 * q], t[4 * q + 1]), pack_bf16x2(t[4 * q + 2], t[4 * q + 3])};
+            float x0 = t[4 * q], x1 = t[4 * q + 1], x2 = t[4 * q + 2], x3 = t[4 * q + 3];
+            if constexpr (ROPE) {
+              // the four columns are two whole pairs (2p, 2p+1), (2p+2, 2p+3)
+              const int row = m0 + 128 * wm + 32 * i + l32, col = col0 + 32 * j + 8 * q + 4 * hi;
+              const int pr = (col % g.rope_d) >> 1;
+              const f32x4 cs = *reinterpret_cast<const f32x4*>(
+                  g.rope_cs + ((int64_t)(row % g.rope_rows) * (g.rope_d >> 1) + pr) * 2);
+              const float y0 = cs[0] * x0 - cs[1] * x1, y1 = cs[1] * x0 + cs[0] * x1;
+              const float y2 = cs[2] * x2 - cs[3] * x3, y3 = cs[3] * x2 + cs[2] * x3;
+              x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+            }
+            const u32x2 v = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
             const uint32_t addr = ew + r * RB + (perm(c >> 4, r) << 4) + (c & 15);
             *(__attribute__((address_space(3))) u32x2*)addr = v;
           } else {
@@ -626,11 +637,13 @@ bool bigtile_form(const GemmArgs& g) {
          al16(g.B) && al16(g.C) && (!g.B2 || (al16(g.B2) && g.n_split % 16 == 0)) &&
          (int64_t)15 * g.lda * 2 + g.K * 2 < (1LL << 31) && (int64_t)15 * g.ldb * 2 + g.K * 2 < (1LL << 31);
 }
-template <int BN>
+template <int BN, bool ROPE = false>
 void launch_big(const GemmArgs& g, hipStream_t st) {
   const unsigned tiles = (unsigned)(((g.M + GB_BM - 1) / GB_BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles, (unsigned)g.batch);
-  if (g.out_bf16)
+  if (ROPE)
+    hipLaunchKernelGGL((gemm_big_kernel<BN, true, true>), grid, dim3(256), 0, st, g);
+  else if (g.out_bf16)
     hipLaunchKernelGGL((gemm_big_kernel<BN, true>), grid, dim3(256), 0, st, g);
   else
     hipLaunchKernelGGL((gemm_big_kernel<BN, false>), grid, dim3(256), 0, st, g);
@@ -673,6 +686,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
     else
       hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, dim3(256), 0, st, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_rope(const GemmArgs& g, hipStream_t st) {
+  // whole pairs per 4-column group, whole 256-column tiles of heads, and a
+  // 16-byte aligned cos/sin table
+  if (g.M <= 0 || g.N <= 0 || g.batch != 1 || !g.out_bf16 || !g.rope_cs || g.rope_rows <= 0 || g.rope_d <= 0 ||
+      g.rope_d % 4 != 0 || 256 % g.rope_d != 0 || g.N % 256 != 0 || ((uintptr_t)g.rope_cs & 15) != 0 ||
+      !bigtile_form(g))
+    return hipErrorNotSupported;
+  launch_big<256, true>(g, st);
   return hipGetLastError();
 }
 

@@ -67,9 +67,17 @@ struct GemmArgs {
   int32_t M, N, K, batch;
   int32_t b_kn;
   int32_t out_bf16;           // bf16 path: store C as bf16 (else fp32)
+  // optional RoPE of the output (launch_gemm_bf16_rope): column n is dim
+  // n % rope_d of a head, row m takes position row rope_cs row m % rope_rows
+  // ([rows, rope_d/2, 2] cos/sin), interleaved pairs (2p, 2p+1)
+  const float* rope_cs; int32_t rope_rows, rope_d;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+// The GEMM with RoPE applied to its bf16 output in the same kernel; returns
+// hipErrorNotSupported (launching nothing) for shapes the fused form does not
+// take, so the caller can run the GEMM and the rotation separately.
+hipError_t launch_gemm_bf16_rope(const GemmArgs& g, hipStream_t st);
 
 // A GEMM and, in one extra workgroup of the same launch, the attention work
 // plan (launch_attn_plan's job); falls back to two launches for GEMM shapes
