@@ -157,3 +157,26 @@ def test_prefill_bf16_two_sequences_after_prefix(form):
         print(f"b={b} rel_l2={err:.3e}")
         assert err <= BF16_TOL
     assert int(cache.err_flags.item()) == 0
+
+
+def test_prefill_bf16_12000_tokens_large_projection_tiles():
+    """B=2 x 6000 tokens: enough rows for the 256-row GEMM tiles on every
+    projection, including [W^DKV ; W^KR] h, whose weight comes in two
+    segments split at row 512 inside a tile (checked through the appended
+    cache rows), and a ragged last row tile (12000 = 46 x 256 + 224)."""
+    s = mi.V3
+    B, L = 2, 6000
+    cfg, cache, w, h, out = _prefill(s, torch.bfloat16, 37, B, L)
+    got = host(out)
+    toks = np.array([0, 255, 256, 4095, 5999])
+    heads = [0, 64, 127]
+    pool = host(cache.pool)
+    bt = cache.block_table.cpu().numpy()
+    for b in range(B):
+        ref, rows = om.prefill(h[b], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=toks, heads=heads)
+        err = rel_l2(got[b][toks][:, heads], ref)
+        rerr = rel_l2(om.paged_gather(pool, bt, b, L, s.page_size), rows)
+        print(f"b={b} out rel_l2={err:.3e} rows rel_l2={rerr:.3e}")
+        assert err <= BF16_TOL
+        assert rerr <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
