@@ -8,15 +8,23 @@
 //   c^Q_raw = W^DQ h,  q^C = W^UQ c^Q,  q^R_raw = W^QR c^Q
 //   q_lat_i = W_i^UK^T q^C_i   (absorption; B given as [K, N] = W_i^UK rows)
 //   o_i = W_i^UV o_lat_i       (W^UV after the weighted sum of latents)
+//   q^R = RoPE(W^QR c^Q)       (explicit prefill: the rotation in the output
+//                               stage of the large-tile kernel)
 //
-// Tiles: 128 x 128 x 64, four waves in a 2 x 2 arrangement, each wave a
-// 64 x 64 block of four 32 x 32 MFMA accumulators.  A and B tiles are staged
-// through double-buffered LDS (row stride 144 B: conflict-free 16-byte
-// fragment reads); the next K slice is fetched into registers while the
-// current one is consumed.  A weight given [K, N] (absorption) is transposed
-// in registers while staging.  Ragged M and N are handled by buffer-resource
-// bounds (out-of-range rows load as zero) and masked stores; K must be a
-// multiple of 64.
+// Three kernels by shape:
+//  * gemm_big_kernel: at least 256 rows and enough tiles to fill the CUs
+//    (the prefill projections): 256 x 256 / 256 x 192 tiles, see below.
+//  * gemm_smallm_bf16_kernel: at most 64 rows, K <= 512 (decode projections).
+//  * gemm_bf16_kernel: everything else, including B given [K, N].  Tiles
+//    128 x 128 x 64, four waves in a 2 x 2 arrangement, each wave a 64 x 64
+//    block of four 32 x 32 MFMA accumulators; A and B tiles staged through
+//    double-buffered LDS (row stride 144 B: conflict-free 16-byte fragment
+//    reads), the next K slice fetched into registers while the current one is
+//    consumed; a weight given [K, N] (absorption) is transposed in registers
+//    while staging.
+// Ragged M and N are handled by buffer-resource bounds (out-of-range rows load
+// as zero) and masked stores; K must be a multiple of 64 (32 for the
+// large-tile kernel).
 #include <algorithm>
 #include <utility>
 
@@ -198,14 +206,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
 // ---- large-tile GEMM (B given [N, K]) ---------------------------------------
 // Output tile 256 x BN (BN = 256 or 192), four waves in a 2 x 2 arrangement,
-// each wave a 128 x BN/2 block of 32 x 32 accumulators in AGPRs, so every
-// 16-byte LDS fragment read feeds BN/64 or 4 MFMAs.  K moves in slices of 32
-// through a ring of four LDS stages filled by direct-to-LDS buffer loads (three
-// slices in flight).  Each 64-byte tile row keeps its four 16-byte chunks at
-// chunk ^ ((row >> 1) & 3), which keeps the fragment reads free of bank
-// conflicts; the loads apply the permutation on the global side.  The
-// product is formed transposed (C^T = B A^T) so each lane holds four
-// consecutive output columns and stores them with one vector store.
+// each wave a 128 x BN/2 block of 32 x 32 accumulators in AGPRs, so each
+// 16-byte fragment read from LDS feeds several MFMAs (an A fragment BN/64, a B
+// fragment 4).  K moves in slices of 32 through a ring of four LDS stages
+// filled by direct-to-LDS buffer loads (three slices in flight).  Each 64-byte
+// tile row keeps its four 16-byte chunks at chunk ^ ((row >> 1) & 3), which
+// keeps the fragment reads free of bank conflicts; the loads apply the
+// permutation on the global side.  The product is formed transposed
+// (C^T = B A^T) so each lane holds four consecutive output columns; the output
+// goes through LDS so that every store writes whole rows.
 constexpr int GB_BM = 256, GB_BK = 32, GB_NST = 4, GB_GM = 4;
 constexpr int GB_ROW = GB_BK * 2;  // bytes per tile row
 
