@@ -202,7 +202,7 @@ def append_inputs(config_id: int, s: Shape, n: int, bf16: bool = True):
 
 # The five workloads the library is measured on.  The decode ones give the
 # context length per sequence; the prefill ones the sequence length.
-CONFIGS = {
+WORKLOADS = {
     1: dict(kind="prefill", shape=TINY, B=1, L=64, dtype="f32"),
     2: dict(kind="decode", shape=V3, B=64, context=4096, s_q=1, dtype="bf16"),
     3: dict(kind="prefill", shape=V3, B=1, L=8192, dtype="bf16"),
@@ -212,7 +212,7 @@ CONFIGS = {
 
 
 def config_context_lens(config_id: int) -> np.ndarray:
-    c = CONFIGS[config_id]
+    c = WORKLOADS[config_id]
     if isinstance(c["context"], tuple):
         lo, hi = c["context"]
         return uniform_lengths(config_id, c["B"], lo, hi)
