@@ -140,3 +140,58 @@ def test_decode_bad_page_and_length_are_flagged():
     assert torch.all(out[1].float() == 0)          # the invalid row is written as zeros
     ref = oracle_decode(inp, seqs=[0])
     assert rel_l2(host(out)[0:1], ref) <= BF16_TOL  # the valid row is unaffected
+
+
+def test_decode_hip_graph_replay_matches_eager():
+    """The decode step (absorption GEMM with the plan, attention, merge + W^UV)
+    issues no memset, copy or synchronisation, so a caller can capture it in a
+    HIP graph.  Every replay (with eager work and synchronisations between
+    replays) must equal the eager result bit for bit, and a replay after the
+    queries change in place must follow them."""
+    import head_latent_attention_06_amd as mla
+    from mla_testutil import dev
+    inp = _case(111, [40, 300, 1000, 2047], 1)
+    cfg, cache, bt, t = decode_setup(inp)
+    max_kv = int(inp.kv_lens.max())
+    B, s_q, H = t["q_nope"].shape[0], t["q_nope"].shape[1], cfg.n_heads
+    out = torch.empty((B, s_q, H, cfg.d_head), dtype=cfg.dtype, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_size(cfg, B, s_q, max_kv), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mla.mla_decode(cfg, cache, t["kv_lens"], max_kv, t["q_nope"], t["q_pe"], t["w_uk"], t["w_uv"], out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert rel_l2(host(eager), oracle_decode(inp)) <= BF16_TOL
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        filler = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"replay {rep}: equal={torch.equal(out, eager)} filler={float(filler):.2f}", flush=True)
+        assert torch.equal(out, eager)
+    # new queries in the same buffers: the replay must use them
+    inp2 = mi.decode_inputs(112, mi.V3, [40, 300, 1000, 2047], 1)
+    t["q_nope"].copy_(dev(inp2.q_nope, torch.bfloat16))
+    t["q_pe"].copy_(dev(inp2.q_pe, torch.bfloat16))
+    step()
+    torch.cuda.synchronize()
+    eager2 = out.clone()
+    assert not torch.equal(eager2, eager)
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager2)
+    assert int(cache.err_flags.item()) == 0
