@@ -195,3 +195,24 @@ def test_decode_hip_graph_replay_matches_eager():
     torch.cuda.synchronize()
     assert torch.equal(out, eager2)
     assert int(cache.err_flags.item()) == 0
+
+
+@pytest.mark.parametrize("page_size", [32, 128])
+def test_decode_other_page_sizes(page_size):
+    """32- and 128-token pages (the tile/page walk with one and four tiles per
+    page), lengths around tile and page edges, two causal queries."""
+    import dataclasses
+    s = dataclasses.replace(mi.V3, page_size=page_size)
+    inp = mi.decode_inputs(121, s, [1, 31, 32, 33, 95, 96, 97, 127, 129, 500, 1100], 2)
+    cfg, cache, bt, t = decode_setup(inp)
+    assert cfg.page_size == page_size
+    out = run_decode(cfg, cache, t, int(inp.kv_lens.max()))
+    torch.cuda.synchronize()
+    got = host(out)
+    ref = oracle_decode(inp)
+    err = rel_l2(got, ref)
+    print(f"page_size={page_size} rel_l2={err:.3e}", flush=True)
+    assert err <= BF16_TOL
+    for b in range(len(inp.kv_lens)):
+        assert rel_l2(got[b], ref[b]) <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0

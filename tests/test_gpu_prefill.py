@@ -180,3 +180,31 @@ def test_prefill_bf16_12000_tokens_large_projection_tiles():
         assert err <= BF16_TOL
         assert rerr <= BF16_TOL
     assert int(cache.err_flags.item()) == 0
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("page_size", [32, 128])
+def test_prefill_bf16_other_page_sizes(form, page_size):
+    """B=2, 200 cached tokens then 130 more, with 32- or 128-token pages."""
+    import dataclasses
+    s = dataclasses.replace(mi.V3, page_size=page_size)
+    w = mi.weights(38, s)
+    h = mi.hidden(38, s, 2, 330)
+    bt, npages = mi.block_table(39, [330, 330], page_size, shuffle=True)
+    cfg = config(s, torch.bfloat16)
+    cfg.prefill_form = form
+    cache = paged_cache(cfg, npages, bt)
+    _prefill(s, torch.bfloat16, 38, 2, 200, w=w, h=h[:, :200], cache=cache, form=form)
+    _, _, _, _, out = _prefill(s, torch.bfloat16, 38, 2, 130, start_pos=200, w=w, h=h[:, 200:], cache=cache,
+                               form=form)
+    toks = np.array([0, 31, 32, 63, 64, 127, 129])
+    pool = host(cache.pool)
+    for b in range(2):
+        ref, rows = om.prefill(h[b], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=200 + toks,
+                               heads=[0, 77, 127])
+        err = rel_l2(host(out)[b][toks][:, [0, 77, 127]], ref)
+        rerr = rel_l2(om.paged_gather(pool, cache.block_table.cpu().numpy(), b, 330, page_size), rows)
+        print(f"page_size={page_size} b={b} rel_l2={err:.3e} rows={rerr:.3e}", flush=True)
+        assert err <= BF16_TOL
+        assert rerr <= BF16_TOL
+    assert int(cache.err_flags.item()) == 0
