@@ -205,6 +205,41 @@ def run_output_projection_bench(steps: int, warmup: int) -> dict:
     return res
 
 
+def run_down_projection_bench(steps: int, warmup: int) -> dict:
+    """[W^DKV ; W^KR] h at the prefill workload's size (B=1, L=8192, d=7168 ->
+    576 columns), through mla_project_kv: the GEMM, then the RMSNorm / RoPE /
+    append of the 8192 new cache rows.  Inputs drawn on the device (seeded
+    N(0,1) h, W ~ N(0, 1/d), unit gain); the rate counts the GEMM's FLOPs over
+    the whole call."""
+    s = mi.V3
+    cfg = mla.Config(**CFG_EXTRA)
+    L = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    h = torch.randn((1, L, s.d_model), device="cuda", generator=g).bfloat16()
+    w = {"w_dkv": (torch.randn((s.d_c, s.d_model), device="cuda", generator=g) * s.d_model ** -0.5).bfloat16(),
+         "w_kr": (torch.randn((s.d_rope, s.d_model), device="cuda", generator=g) * s.d_model ** -0.5).bfloat16(),
+         "g_kv": torch.ones((s.d_c,), device="cuda").bfloat16()}
+    bt, npages = mi.block_table(3, [L], s.page_size, shuffle=True)
+    cache = mla.PagedCache(torch.zeros((npages, s.page_size, cfg.row), dtype=torch.bfloat16, device="cuda"),
+                           torch.from_numpy(bt).cuda())
+    ws = torch.empty(max(mla.mla_project_kv_workspace_size(cfg, 1, L), 256), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        mla.mla_project_kv(cfg, cache, w, h, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mla.mla_project_kv(cfg, cache, w, h, ws=ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    flops = 2 * L * (s.d_c + s.d_rope) * s.d_model
+    del h, w, cache, ws
+    torch.cuda.empty_cache()
+    return {"workload": "down-projection + append, B=1, L=8192, d=7168 -> 576 (c^KV 512 + k^R 64), bf16",
+            "us": round(us, 1), "gemm_flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "frac_mfma": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def run_other_decode(steps: int, warmup: int) -> dict:
     """The long-context (B=4 x 131072) and ragged (B=128, context ~ U{1..32768},
     s_q=2) decode workloads.  Cache, queries and weights are drawn on the device
@@ -379,6 +414,7 @@ def main():
         res["other_decode"] = run_other_decode(max(10, args.steps // 4), max(20, args.warmup // 4))
     if not args.no_prefill:
         res["prefill"] = run_prefill_summary(args)
+        res["down_projection"] = run_down_projection_bench(20, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d["inp"], args.cpu_seconds)
     print(json.dumps(res), flush=True)
