@@ -149,6 +149,14 @@ mla_status prefill_form(const mla_config* c, bool bf16, int32_t L, int32_t start
   return MLA_OK;
 }
 
+// [W^DKV ; W^KR] h has few output columns (d_c + d_rope): with too few
+// 256 x 192 tiles to fill the chip, the reduction over d_model runs as two
+// halves in one launch of twice the tiles and the append adds them.
+int kv_ksplit(const mla_config* c, bool bf16, int64_t T) {
+  const int64_t row = c->d_c + c->d_rope;
+  return bf16 && c->d_model % 128 == 0 && 2 * ((T + 255) / 256) * ((row + 191) / 192) <= 256 ? 2 : 1;
+}
+
 struct PrefillWs {
   float *kv_raw, *cq_raw, *qr_raw, *rope_cs, *part_ml;
   void *cq, *qc, *q_abs, *o_lat, *part_o;
@@ -166,7 +174,7 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, bool use_explicit, int3
   const int64_t T = (int64_t)B * L, H = c->n_heads, row = c->d_c + c->d_rope;
   const size_t e = bf16 ? 2 : 4;
   p.rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
-  p.kv_raw = (float*)cv.take(T * row * 4);
+  p.kv_raw = (float*)cv.take(kv_ksplit(c, bf16, T) * T * row * 4);
   p.cq_raw = (float*)cv.take(T * c->d_cq * 4);
   p.cq = cv.take(T * c->d_cq * e);
   p.qc = cv.take(T * H * c->d_head * e);
@@ -196,11 +204,12 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, bool use_explicit, int3
   return p;
 }
 
-size_t project_kv_layout(const mla_config* c, int32_t B, int32_t L, void* ws, float** rope_cs, float** kv_raw) {
+size_t project_kv_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, void* ws, float** rope_cs,
+                         float** kv_raw) {
   Carve cv(ws);
   const int64_t T = (int64_t)B * L;
   *rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
-  *kv_raw = (float*)cv.take(T * (c->d_c + c->d_rope) * 4);
+  *kv_raw = (float*)cv.take(kv_ksplit(c, bf16, T) * T * (c->d_c + c->d_rope) * 4);
   return cv.off;
 }
 
@@ -234,7 +243,8 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   const int64_t T = (int64_t)B * L;
   const int row = c->d_c + c->d_rope;
   MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, rope_params(c), st));
-  GemmArgs g = gemm(h, c->d_model, 0, w->w_dkv, c->d_model, 0, kv_raw, row, 0, (int)T, row, c->d_model, 1, false,
+  const int ks = kv_ksplit(c, bf16, T), kh = c->d_model / ks;
+  GemmArgs g = gemm(h, c->d_model, kh, w->w_dkv, c->d_model, kh, kv_raw, row, T * row, (int)T, row, kh, ks, false,
                     false);
   g.B2 = w->w_kr;
   g.n_split = c->d_c;
@@ -246,6 +256,7 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   a.seq_idx = nullptr; a.pos = nullptr;
   a.n = (int32_t)T; a.n_seqs = B; a.L = L; a.start_pos = start_pos;
   a.in_f32 = 1;
+  a.part_stride = ks == 2 ? T * row : 0;
   a.rope_cs = rope_cs;
   a.pool = k->pool; a.num_pages = k->num_pages;
   a.block_table = k->block_table; a.max_pages = k->max_pages_per_seq; a.page_size = c->page_size;
@@ -409,7 +420,7 @@ mla_status mla_project_kv_workspace_size(const mla_config* cfg, int32_t B, int32
   if (s != MLA_OK) return s;
   if (!bytes || B < 0 || L < 0) return MLA_ERR_INVALID_ARG;
   float *a, *b;
-  *bytes = project_kv_layout(cfg, B, L, nullptr, &a, &b);
+  *bytes = project_kv_layout(cfg, bf16, B, L, nullptr, &a, &b);
   return MLA_OK;
 }
 
@@ -426,7 +437,7 @@ mla_status mla_project_kv(const mla_config* cfg, const mla_kv_cache* cache, cons
   if (B > (1 << 20) || (int64_t)start_pos + L > (int64_t)cache->max_pages_per_seq * cfg->page_size)
     return MLA_ERR_OUT_OF_RANGE;
   float *rope_cs, *kv_raw;
-  if (project_kv_layout(cfg, B, L, ws, &rope_cs, &kv_raw) > ws_bytes) return MLA_ERR_WORKSPACE;
+  if (project_kv_layout(cfg, bf16, B, L, ws, &rope_cs, &kv_raw) > ws_bytes) return MLA_ERR_WORKSPACE;
   return project_and_append(cfg, bf16, cache, w, h, B, L, start_pos, rope_cs, kv_raw, (hipStream_t)stream);
 }
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
   const bf16* A = (const bf16*)g.A + z * g.strideA;
   const bf16* B = (const bf16*)g.B + z * g.strideB;
-  const bf16* B2 = (const bf16*)g.B2;
+  const bf16* B2 = g.B2 ? (const bf16*)g.B2 + z * g.strideB : nullptr;
 
   // --- staging assignment -------------------------------------------------
   // A: chunk c = tid + 256*i (i < 4): row c/8, k chunk c%8 (16 B each).
@@ -293,7 +293,7 @@ void gemm_big_kernel(GemmArgs g) {
     const unsigned char* p;
     int rows;
     if (g.B2 && n >= g.n_split) {
-      p = (const unsigned char*)g.B2 + (int64_t)(n - g.n_split) * ldb2;
+      p = (const unsigned char*)g.B2 + (int64_t)z * g.strideB * 2 + (int64_t)(n - g.n_split) * ldb2;
       rows = min(16, g.N - n);
     } else {
       p = B + (int64_t)n * ldb2;
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const int z = blockIdx.y;
   const float* A = (const float*)g.A + z * g.strideA;
   const float* B = (const float*)g.B + z * g.strideB;
-  const float* B2 = (const float*)g.B2;
+  const float* B2 = g.B2 ? (const float*)g.B2 + z * g.strideB : nullptr;
   float accv = 0.f;
   for (int k0 = 0; k0 < g.K; k0 += 16) {
     const int m = m0 + ty, k = k0 + tx;

@@ -62,7 +62,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 struct GemmArgs {
   const void* A; int64_t lda, strideA;
   const void* B; int64_t ldb, strideB;
-  const void* B2; int32_t n_split;
+  const void* B2; int32_t n_split;  // rows n >= n_split of B come from B2 (row n - n_split), same ldb and strideB
   void* C; int64_t ldc, strideC;
   int32_t M, N, K, batch;
   int32_t b_kn;
@@ -108,6 +108,8 @@ struct AppendArgs {
   const int32_t* seq_idx; const int32_t* pos;
   int32_t n, n_seqs, L, start_pos;
   int32_t in_f32;                    // ckv / kr are fp32 (else cfg dtype)
+  int64_t part_stride;               // in_f32: each value is the sum of two partial products, the second
+                                     // part_stride elements after the first (0: one product)
   const float* rope_cs;              // optional [L, d_rope/2, 2] cos/sin for implicit positions
   void* pool; int64_t num_pages;
   const int32_t* block_table; int32_t max_pages, page_size;

@@ -75,17 +75,23 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int row = a.d_c + a.d_rope;
   TOUT* dst = (TOUT*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * row;
   const int64_t ci = (int64_t)i * a.ld_ckv, ki = (int64_t)i * a.ld_kr;
+  // the projection, as one product or the sum of its two k-halves
+  const auto in = [&](const void* p, int64_t o) {
+    float x = ld_as_f32<TIN>(p, o);
+    if (a.part_stride) x += ld_as_f32<TIN>(p, o + a.part_stride);
+    return x;
+  };
 
   // RMSNorm of the latent
   float ss = 0.f;
   for (int d = lane; d < a.d_c; d += 64) {
-    const float x = ld_as_f32<TIN>(a.ckv, ci + d);
+    const float x = in(a.ckv, ci + d);
     ss += x * x;
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)a.d_c + a.eps);
   for (int d = lane; d < a.d_c; d += 64) {
-    const float x = ld_as_f32<TIN>(a.ckv, ci + d);
+    const float x = in(a.ckv, ci + d);
     const float g = ld_as_f32<TOUT>(a.g_kv, d);
     dst[d] = from_f32<TOUT>(x * inv * g);
   }
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     } else {
       rope_cos_sin(pos, p, a.d_rope, a.rope, c, s);
     }
-    const float x0 = ld_as_f32<TIN>(a.kr, ki + 2 * p), x1 = ld_as_f32<TIN>(a.kr, ki + 2 * p + 1);
+    const float x0 = in(a.kr, ki + 2 * p), x1 = in(a.kr, ki + 2 * p + 1);
     dst[a.d_c + 2 * p] = from_f32<TOUT>(c * x0 - s * x1);
     dst[a.d_c + 2 * p + 1] = from_f32<TOUT>(s * x0 + c * x1);
   }

@@ -49,3 +49,29 @@ def test_project_kv_f32_tiny():
         c, kr = om.latent_rows(h[b], w["w_dkv"], w["g_kv"], w["w_kr"], np.arange(50), s.rms_eps, s.rope_base)
         rows = om.paged_gather(pool, bt, b, 50, s.page_size)
         assert rel_l2(rows, np.concatenate([c, kr], 1)) <= F32_TOL
+
+
+@pytest.mark.parametrize("B,L", [(2, 4096), (1, 10752), (1, 10753)])
+def test_project_kv_bf16_large(B, L):
+    """Token counts that take the 256-row GEMM tiles: up to 10752 tokens the
+    reduction over d_model runs as two halves summed by the append, from
+    10753 on as one (the boundary sits on both sides); sampled rows include
+    tile edges and the ragged last tile."""
+    s = mi.V3
+    cfg = config(s)
+    w = mi.weights(53, s)
+    h = mi.hidden(53 + L, s, B, L)
+    bt, npages = mi.block_table(53, [L] * B, s.page_size, shuffle=True)
+    cache = paged_cache(cfg, npages, bt)
+    wd = {k: dev(w[k]) for k in ("w_dkv", "w_kr", "g_kv")}
+    print(f"project_kv B={B} L={L}", flush=True)
+    mla.mla_project_kv(cfg, cache, wd, dev(h))
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    pool = host(cache.pool)
+    toks = np.unique(np.array([0, 1, 255, 256, 4095, L // 2, L - 257, L - 256, L - 2, L - 1]) % L)
+    for b in range(B):
+        c, kr = om.latent_rows(h[b][toks], w["w_dkv"], w["g_kv"], w["w_kr"], toks, s.rms_eps, s.rope_base)
+        rows = np.stack([pool[om.paged_slot(bt, b, int(t), s.page_size)] for t in toks])
+        assert rel_l2(rows[:, :s.d_c], c) <= BF16_TOL
+        assert rel_l2(rows[:, s.d_c:], kr) <= BF16_TOL
