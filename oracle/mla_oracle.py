@@ -46,6 +46,14 @@ design notes of the repository):
   * Decode: the step's s_q new tokens are already cached; query s of a
     sequence with kv_len cached rows sits at position kv_len - s_q + s and
     attends to rows j <= that position.
+  * FP8 latent cache (optional; the hnwysp.cn digest's FP8 passage fixes only
+    the granularity: activations are quantised per 1 x 128 tile, each tile
+    with its own scale).  The format is OCP E4M3 ("e4m3fn": 4 exponent bits,
+    bias 7, 3 mantissa bits, largest finite 448, no infinities).  Each
+    128-value tile of c^KV gets a power-of-two scale 2^e, e the smallest
+    integer with max|x| <= 448 * 2^e, and codes round x / 2^e to the nearest
+    E4M3 value, ties to even.  The decision is taken on the value rounded to
+    float32.  k^R is not quantised.
 """
 from __future__ import annotations
 
@@ -320,6 +328,84 @@ def prefill(h, w, n_heads: int, eps: float, base: float, scale: float, start_pos
     o = explicit_attention(q_c, q_r, rows[:, :d_c], rows[:, d_c:], w["w_uk"], w["w_uv"],
                            pos[tokens], eff_scale, heads=heads)
     return o, new_rows
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache: E4M3 codes with one power-of-two scale per 1 x 128 tile
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+FP8_TILE = 128
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of E4M3 codes (uint8): sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent field 0 is subnormal (m/8 * 2^-6); exponent
+    15 with mantissa 7 is NaN; there is no infinity."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code to each x (|x| <= 448), ties to the even code.
+
+    Within a binade [2^k, 2^(k+1)), k >= -6, neighbouring values are 2^(k-3)
+    apart; below 2^-6 (subnormals) they are 2^-9 apart.  The magnitude is
+    rounded to a multiple of that spacing (numpy's rint rounds halves to even,
+    and an even multiple is an even mantissa), and a value that rounds up to
+    the next power of two is that power's code.  The sign bit is kept, so
+    small negative values give -0 (0x80)."""
+    x = _f64(x)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("E4M3 encoding takes finite |x| <= 448")
+    a = np.abs(x)
+    k = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    k = np.where(a >= 2.0 ** -6, k, -6.0)
+    # log2 near a power of two may land one off: fix k so 2^k <= a < 2^(k+1)
+    k = np.where((a >= 2.0 ** -6) & (2.0 ** k > a), k - 1, k)
+    k = np.where((a >= 2.0 ** -6) & (2.0 ** (k + 1) <= a), k + 1, k)
+    step = 2.0 ** (k - 3)
+    q = np.rint(a / step) * step  # the rounded magnitude
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = q < 2.0 ** -6
+    code = np.where(sub, np.rint(q / 2.0 ** -9), code)
+    kq = np.floor(np.log2(np.where(sub, 1.0, q)))
+    kq = np.where(~sub & (2.0 ** kq > q), kq - 1, kq)
+    mant = np.rint((q / 2.0 ** kq - 1.0) * 8.0)
+    code = np.where(sub, code, ((kq + 7) * 8 + mant)).astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_tile_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (e = 0 for an all-zero tile)."""
+    amax = _f64(amax)
+    e = np.ceil(np.log2(np.where(amax > 0, amax, E4M3_MAX) / E4M3_MAX))
+    e = np.where(amax > E4M3_MAX * 2.0 ** e, e + 1, e)
+    e = np.where((amax > 0) & (amax <= E4M3_MAX * 2.0 ** (e - 1)), e - 1, e)
+    return e.astype(np.int64)
+
+
+def quantize_latent_fp8(c):
+    """c [..., d_c] -> (codes uint8 [..., d_c], tile exponents int [..., d_c/128],
+    dequantised float64 [..., d_c]).  Codes are decided on float32(c)."""
+    x = np.asarray(c, dtype=np.float32).astype(F64)
+    tiles = x.reshape(x.shape[:-1] + (x.shape[-1] // FP8_TILE, FP8_TILE))
+    e = fp8_tile_exponent(np.max(np.abs(tiles), axis=-1))
+    scale = 2.0 ** e[..., None]
+    codes = e4m3_encode(tiles / scale)
+    deq = e4m3_value(codes) * scale
+    return codes.reshape(x.shape), e, deq.reshape(x.shape)
+
+
+def cache_row_fp8(c_raw, k_raw, g_kv, pos, eps: float, base: float, yarn=None):
+    """A cached row in the FP8 format: (codes, tile exponents, k^R, and the row
+    the attention reads, [dequantised RMSNorm(c_raw) ; RoPE(k_raw, pos)])."""
+    codes, e, c_deq = quantize_latent_fp8(rms_norm(c_raw, g_kv, eps))
+    k_r = rope(k_raw, pos, base, yarn)
+    return codes, e, k_r, np.concatenate([c_deq, k_r], axis=-1)
 
 
 # ---------------------------------------------------------------------------
