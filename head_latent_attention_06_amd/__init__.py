@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_RANGE, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
 MLA_F32, MLA_BF16 = 0, 1
 PREFILL_AUTO, PREFILL_ABSORBED, PREFILL_EXPLICIT = 0, 1, 2
-ABI_VERSION = 3  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
+ABI_VERSION = 4  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
 MLA_FLAG_BAD_PAGE, MLA_FLAG_BAD_POS, MLA_FLAG_BAD_LEN, MLA_FLAG_BAD_SEQ = 1, 2, 4, 8
 
 
@@ -36,7 +36,7 @@ class _Config(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("prefill_form", ctypes.c_int32),
                 ("yarn_s", ctypes.c_float), ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float),
-                ("yarn_orig_ctx", ctypes.c_int32)]
+                ("yarn_orig_ctx", ctypes.c_int32), ("kv_fp8", ctypes.c_int32)]
 
 
 class _Cache(ctypes.Structure):
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         CP, KP, WP = ctypes.POINTER(_Config), ctypes.POINTER(_Cache), ctypes.POINTER(_Weights)
         sig = {
             "mla_abi_version": (I32, []),
+            "mla_cache_row_bytes": (ctypes.c_int64, [CP]),
             "mla_status_string": (ctypes.c_char_p, [I32]),
             "mla_cache_append": (I32, [CP, KP, P, P, P, P, P, I32, I32, P]),
             "mla_project_kv_workspace_size": (I32, [CP, I32, I32, ctypes.POINTER(SZ)]),
@@ -115,17 +116,28 @@ class Config:
     yarn_alpha: float = 1.0
     yarn_beta: float = 32.0
     yarn_orig_ctx: int = 4096
+    # FP8 latent cache: E4M3 codes of c^KV with a power-of-two scale per 128
+    # values, k^R in bf16; 656-byte rows (bf16 compute only)
+    kv_fp8: bool = False
 
     @property
     def row(self) -> int:
         return self.d_c + self.d_rope
+
+    @property
+    def row_bytes(self) -> int:
+        """Bytes per cached row (a uint8 pool of [pages, page_size, row_bytes] fits any config)."""
+        n = lib().mla_cache_row_bytes(ctypes.byref(self._c()))
+        if n < 0:
+            raise MLAError(MLA_ERR_INVALID_ARG, "mla_cache_row_bytes")
+        return n
 
     def _c(self) -> _Config:
         scale = self.softmax_scale if self.softmax_scale is not None else (self.d_head + self.d_rope) ** -0.5
         dt = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32}[self.dtype]
         return _Config(self.n_heads, self.d_head, self.d_rope, self.d_c, self.d_cq, self.d_model, self.page_size,
                        scale, self.rope_base, self.rms_eps, dt, self.prefill_form, self.yarn_s, self.yarn_alpha,
-                       self.yarn_beta, self.yarn_orig_ctx)
+                       self.yarn_beta, self.yarn_orig_ctx, int(self.kv_fp8))
 
 
 @dataclass

@@ -13,6 +13,7 @@ using namespace mla;
 namespace {
 
 constexpr int ATTN_SPLIT_PAGES = 1536;  // page ids one attention workgroup stages in LDS
+constexpr int ATTN_SPLIT_PAGES_FP8 = 512;  // the same with an FP8 cache (its staging takes the LDS)
 constexpr int DECODE_TARGET_ITEMS = 256;  // about one workgroup per CU for even batches
 constexpr int RAGGED_FACTOR = 4;          // the plan uses 4x as many chunks for ragged ones
 constexpr int MIN_CHUNK = 256;
@@ -57,6 +58,8 @@ mla_status check_cfg(const mla_config* c, bool* bf16) {
   if (!(c->softmax_scale > 0.f) || !(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return MLA_ERR_INVALID_ARG;
   if (c->prefill_form < MLA_PREFILL_AUTO || c->prefill_form > MLA_PREFILL_EXPLICIT) return MLA_ERR_INVALID_ARG;
   if (c->yarn_s > 1.f && !(c->yarn_beta > c->yarn_alpha && c->yarn_orig_ctx > 0)) return MLA_ERR_INVALID_ARG;
+  if (c->kv_fp8 != 0 && c->kv_fp8 != 1) return MLA_ERR_INVALID_ARG;
+  if (c->kv_fp8 && c->dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   if (c->page_size % 32 != 0 || (c->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
   if (c->dtype == MLA_BF16) {
     *bf16 = true;
@@ -82,7 +85,7 @@ mla_status check_cache(const mla_config* c, const mla_kv_cache* k) {
 }
 
 int32_t max_chunk_keys(const mla_config* c) {
-  const int64_t m = (int64_t)(ATTN_SPLIT_PAGES - 1) * c->page_size;
+  const int64_t m = (int64_t)((c->kv_fp8 ? ATTN_SPLIT_PAGES_FP8 : ATTN_SPLIT_PAGES) - 1) * c->page_size;
   return (int32_t)(m > (1 << 30) ? (1 << 30) : m);
 }
 
@@ -264,6 +267,7 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   a.d_c = c->d_c; a.d_rope = c->d_rope;
   a.eps = c->rms_eps; a.rope = rope_params(c);
   a.bf16_cache = bf16 ? 1 : 0;
+  a.fp8_cache = c->kv_fp8;
   MLA_HIP(launch_append(a, st));
   return MLA_OK;
 }
@@ -276,6 +280,7 @@ AttnArgs attn_args(const mla_config* c, const mla_kv_cache* k, const void* q_lat
   a.q_rope = q_rope;
   a.ld_r = ld_r;
   a.pool = k->pool;
+  a.fp8 = c->kv_fp8;
   a.block_table = k->block_table;
   a.num_pages = k->num_pages;
   a.max_pages = k->max_pages_per_seq;
@@ -344,6 +349,7 @@ mla_status prefill_explicit(const mla_config* c, const mla_kv_cache* k, const ml
   g.pool = k->pool; g.num_pages = k->num_pages;
   g.block_table = k->block_table; g.max_pages = k->max_pages_per_seq; g.page_size = c->page_size;
   g.B = B; g.kv_end = kv_end; g.row = row;
+  g.fp8 = c->kv_fp8;
   g.err_flags = k->err_flags;
   g.out = p.kvg;
   MLA_HIP(launch_gather_rows(g, st));
@@ -374,6 +380,13 @@ mla_status prefill_explicit(const mla_config* c, const mla_kv_cache* k, const ml
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int64_t mla_cache_row_bytes(const mla_config* cfg) {
+  bool bf16;
+  if (check_cfg(cfg, &bf16) != MLA_OK) return -1;
+  if (cfg->kv_fp8) return 656;
+  return (int64_t)(cfg->d_c + cfg->d_rope) * (bf16 ? 2 : 4);
+}
 
 const char* mla_status_string(mla_status s) {
   switch (s) {
@@ -411,6 +424,7 @@ mla_status mla_cache_append(const mla_config* cfg, const mla_kv_cache* cache, co
   a.d_c = cfg->d_c; a.d_rope = cfg->d_rope;
   a.eps = cfg->rms_eps; a.rope = rope_params(cfg);
   a.bf16_cache = bf16 ? 1 : 0;
+  a.fp8_cache = cfg->kv_fp8;
   return launch_append(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -34,6 +34,15 @@
 //    a tile's max exceeds it by more than 8 (p <= 256 stays exact in fp32),
 //    so the 256-register O^T accumulator (kept in AGPRs) is rescaled rarely.
 //    Row max / sum across the two lane halves use v_permlane32_swap.
+//
+// FP8 cache (the same kernel, FP8 = true): rows are 656 bytes, c^KV as 512
+// E4M3 codes, then k^R as 64 bf16, then four fp32 scales 2^e, one per
+// 128-value tile of c^KV.  Each tile's codes and k^R (640 bytes a row) move
+// by direct-to-LDS loads into one of two staging slots, one tile ahead; the
+// workgroup then decodes every value once (v_cvt_scalef32_pk_bf16_fp8: two
+// codes per instruction, the power-of-two scale exact) into the bf16 stage
+// layout above, so the QK and PV code is the same for both caches.  Three
+// bf16 stages then suffice (two read, one written per pass).
 #include <math.h>
 
 #include "mla_device.h"
@@ -54,6 +63,16 @@ constexpr int DMA_PER_THREAD = STAGE / 16 / 256; // 9 16-byte loads per thread p
 constexpr int WG_HEADS = 128;
 constexpr int MAX_SPLIT_PAGES = 1536;            // page ids of one split, staged in LDS
 constexpr int FLAG_BAD_PAGE = 1, FLAG_BAD_LEN = 4;
+// FP8 cache
+constexpr int F_RB = 656;                        // bytes per cached row
+constexpr int F_SROW = 640;                      // bytes staged per row: codes, then k^R
+constexpr int F_SCALE = 640;                     // row offset of the four tile scales
+constexpr int F_STAGE = TILE * F_SROW;           // 20480 bytes per staging slot
+constexpr int F_NSLOT = 2, F_NSTAGE = 3;
+constexpr int F_DMA = F_STAGE / 16 / 256;        // 5 16-byte loads per thread per tile
+constexpr int F_SPLIT_PAGES = 512;               // page ids of one split (LDS budget)
+static_assert(F_NSTAGE * STAGE + F_NSLOT * F_STAGE + F_SPLIT_PAGES * 4 <= NSTAGE * STAGE + MAX_SPLIT_PAGES * 4,
+              "FP8 LDS layout exceeds the bf16 one");
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.0f;
 
@@ -115,10 +134,26 @@ __device__ __forceinline__ void scale_acc_tuple(f32x16& t, float alpha) {
 #undef MLA_SCALE1
 }
 
+__device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+// two E4M3 codes (bytes 2W, 2W+1 of src) times 2^e (the scale's exponent) as bf16
+template <bool W>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t src, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, scale, W));
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
-  __shared__ int split_pages[MAX_SPLIT_PAGES];
+  constexpr int NST = FP8 ? F_NSTAGE : NSTAGE;             // bf16 tile stages
+  constexpr int SPLIT_PAGES = FP8 ? F_SPLIT_PAGES : MAX_SPLIT_PAGES;
+  constexpr int NDMA = FP8 ? F_DMA : DMA_PER_THREAD;
+  constexpr int RBG = FP8 ? F_RB : RB;                     // bytes per cached row
+  __shared__ __attribute__((aligned(16))) unsigned char smem[FP8 ? F_NSTAGE * STAGE + F_NSLOT * F_STAGE
+                                                                 : NSTAGE * STAGE];
+  __shared__ int split_pages[SPLIT_PAGES];
   __shared__ u32x4 p_xchg[4 * 2 * 64];   // P^T fragments [head block][k step][lane]
   __shared__ float alpha_xchg[4][32];    // per head: rescale factor of the current tile
   __shared__ float lsum_xchg[4][32];     // per head: softmax sum of the chunk
@@ -149,8 +184,8 @@ void attn_bf16_kernel(AttnArgs a) {
   // not queue behind them
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int pg_first = k0 / a.page_size;
-  const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= MAX_SPLIT_PAGES (host plan)
-  constexpr int PAGES_PER_THREAD = MAX_SPLIT_PAGES / 256;
+  const int n_pages = (k1 - 1) / a.page_size - pg_first + 1;  // <= SPLIT_PAGES (host plan)
+  constexpr int PAGES_PER_THREAD = SPLIT_PAGES / 256;
   int pid[PAGES_PER_THREAD];
 #pragma unroll
   for (int k = 0; k < PAGES_PER_THREAD; ++k) {
@@ -164,12 +199,15 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // ---- tile loads: wave w's instruction i covers LDS chunks (4i + w)*64 + lane
   // of the stage; LDS chunk P holds key row P / 72, row chunk (P % 72) ^ kswz(row).
-  int32_t dma_off[DMA_PER_THREAD];
+  // FP8: of the staging slot, P / 40 and (P % 40) ^ kswz(row) of the row's
+  // 40 chunks (32 of codes, 8 of k^R).
+  int32_t dma_off[NDMA];
 #pragma unroll
-  for (int i = 0; i < DMA_PER_THREAD; ++i) {
+  for (int i = 0; i < NDMA; ++i) {
     const int P = (4 * i + wave) * 64 + lane;
-    const int r = P / 72, c = (P % 72) ^ kswz(P / 72);
-    dma_off[i] = r * RB + c * 16;
+    constexpr int CPR = FP8 ? F_SROW / 16 : RB / 16;
+    const int r = P / CPR, c = (P % CPR) ^ kswz(P / CPR);
+    dma_off[i] = r * RBG + c * 16;
   }
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
   // Issue cursor: the next tile to load sits at key offset cur_off of page
@@ -178,7 +216,7 @@ void attn_bf16_kernel(AttnArgs a) {
   int cur_slot = 0, cur_off = k0 % a.page_size, cur_tile = 0;
   const int ntiles = (k1 - k0 + TILE - 1) / TILE;
   const uint64_t pool_addr = (uint64_t)(uintptr_t)a.pool;
-  const uint32_t page_bytes = (uint32_t)a.page_size * RB;
+  const uint32_t page_bytes = (uint32_t)a.page_size * RBG;
   const uint32_t num_pages = (uint32_t)min<int64_t>(a.num_pages, 0x7fffffff);
   bool bad_page = false;  // reported once, after the loop
   struct TileDma {
@@ -196,10 +234,11 @@ void attn_bf16_kernel(AttnArgs a) {
     // rows of the tile are contiguous within one page; rows past k1 (and a
     // bad page) lie outside the resource and load as zeros
     const int kb = k0 + cur_tile * TILE;
-    const uint64_t addr = pool_addr + (uint64_t)(pok ? page : 0u) * page_bytes + (uint32_t)cur_off * RB;
+    const uint64_t addr = pool_addr + (uint64_t)(pok ? page : 0u) * page_bytes + (uint32_t)cur_off * RBG;
     TileDma d;
-    d.r = make_rsrc((const void*)(uintptr_t)addr, (real && pok) ? min(TILE, k1 - kb) * RB : 0);
-    d.dst = smem_addr + (cur_tile % NSTAGE) * STAGE + wave * 1024;
+    d.r = make_rsrc((const void*)(uintptr_t)addr, (real && pok) ? min(TILE, k1 - kb) * RBG : 0);
+    d.dst = FP8 ? smem_addr + F_NSTAGE * STAGE + (cur_tile % F_NSLOT) * F_STAGE + wave * 1024
+                : smem_addr + (cur_tile % NSTAGE) * STAGE + wave * 1024;
     cur_tile += 1;
     cur_off += TILE;
     if (cur_off == a.page_size) {
@@ -210,17 +249,63 @@ void attn_bf16_kernel(AttnArgs a) {
     return d;
   };
   // page id at the cursor (a stale id past the chunk: its tile is empty)
-  auto cursor_page = [&]() { return split_pages[min(cur_slot, MAX_SPLIT_PAGES - 1)]; };
+  auto cursor_page = [&]() { return split_pages[min(cur_slot, SPLIT_PAGES - 1)]; };
   auto issue_next = [&](int page_id) {
     const TileDma d = prep_tile(page_id);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_THREAD; ++i) dma16(d.r, d.dst + i * 4096, dma_off[i]);
+    for (int i = 0; i < NDMA; ++i) dma16(d.r, d.dst + i * 4096, dma_off[i]);
+    return d;
   };
 
+  // ---- FP8: decoding of a staged tile into a bf16 stage.  Thread (row
+  // r = lane & 31, part p = 2 wave + hi) takes codes 64p .. 64p+63 of row r
+  // (all in 128-value tile `wave`, scale `sc`) and k^R chunk p.  Per step:
+  // 0..3 read code chunk q, 4 read the k^R chunk (into cvb), 5 + 2q + h decode
+  // and store half h of chunk q, 13 store the k^R chunk.
+  // Row offsets of this thread's staged and decoded rows (part p's first chunk
+  // folded in), and 16 * kswz(row): a chunk index 8a + j (j < 8) swizzles to
+  // 8a + (j ^ kswz), so each address is base + (16 j ^ cv_k16).  The XOR is
+  // redone at every access (cv_k16 is opaque to the compiler) rather than
+  // kept as 14 loop-invariant addresses, which would not fit the registers.
+  const int cv_r = lane & 31, cv_p = 2 * wave + hi;
+  const int cv_rd = cv_r * F_SROW + 128 * (cv_p >> 1), cv_wr = cv_r * RB + 128 * cv_p;
+  const int cv_k16 = 16 * kswz(lane & 31);
+  u32x4 cvb = {0u, 0u, 0u, 0u};
+  auto cv_step = [&](int step, const unsigned char* F, unsigned char* S, float sc) {
+    if constexpr (FP8) {
+      int k16 = cv_k16;
+      asm volatile("" : "+v"(k16));
+      if (step < 4) {  // chunk 4p + step = 8 (p >> 1) + (4 (p & 1) + step)
+        cvb = *(const u32x4*)(F + cv_rd + ((16 * (4 * (cv_p & 1) + step)) ^ k16));
+      } else if (step < 12) {
+        const int q = (step - 4) >> 1, h = (step - 4) & 1;
+        u32x4 o;
+        o[0] = fp8x2_bf16<false>(cvb[2 * h], sc);
+        o[1] = fp8x2_bf16<true>(cvb[2 * h], sc);
+        o[2] = fp8x2_bf16<false>(cvb[2 * h + 1], sc);
+        o[3] = fp8x2_bf16<true>(cvb[2 * h + 1], sc);
+        *(u32x4*)(S + cv_wr + ((16 * (2 * q + h)) ^ k16)) = o;
+      } else if (step == 12) {  // k^R chunk 32 + p of the staged row
+        cvb = *(const u32x4*)(F + cv_r * F_SROW + 512 + ((16 * cv_p) ^ k16));
+      } else {                  // bf16 chunk 64 + p
+        *(u32x4*)(S + cv_r * RB + 1024 + ((16 * cv_p) ^ k16)) = cvb;
+      }
+    }
+  };
+  auto scale_of = [&](const TileDma& d) { return buf_ld4f(d.r, cv_r * F_RB + F_SCALE + 4 * wave); };
+  float scl_cv = 0.f, scl_nx = 0.f;  // scales of the tile decoded next, and of the one after
+
   // ---- tiles 0 .. DEPTH-1 (possibly empty), then the queries: one burst
-  issue_next(split_pages[0]);
+  // (FP8: tiles 0 and 1 are decoded once they land, tile 2 stays in flight)
+  TileDma d0 = issue_next(split_pages[0]);
+  if constexpr (FP8) {
+    scl_cv = scale_of(d0);
+    d0 = issue_next(cursor_page());
+    scl_nx = scale_of(d0);
+  } else {
 #pragma unroll
-  for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
+    for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
+  }
   // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
   // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
   u32x4 qf[36];
@@ -244,6 +329,25 @@ void attn_bf16_kernel(AttnArgs a) {
                "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]));
   asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
                "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
+  if constexpr (FP8) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    const unsigned char* F0 = smem + F_NSTAGE * STAGE;
+#pragma unroll
+    for (int t0 = 0; t0 < 2; ++t0) {
+      // steps in order: each chunk is read, then decoded in two halves
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cv_step(q, F0 + t0 * F_STAGE, smem + t0 * STAGE, t0 ? scl_nx : scl_cv);
+        cv_step(4 + 2 * q, F0 + t0 * F_STAGE, smem + t0 * STAGE, t0 ? scl_nx : scl_cv);
+        cv_step(5 + 2 * q, F0 + t0 * F_STAGE, smem + t0 * STAGE, t0 ? scl_nx : scl_cv);
+      }
+      cv_step(12, F0 + t0 * F_STAGE, smem + t0 * STAGE, 0.f);
+      cv_step(13, F0 + t0 * F_STAGE, smem + t0 * STAGE, 0.f);
+    }
+    __syncthreads();  // staging slot 0 is free again, tiles 0 and 1 are in place
+    scl_cv = scale_of(issue_next(cursor_page()));
+  }
   // page of the next tile to issue, fetched one tile early to keep the LDS
   // latency off the issue path
   int next_page = cursor_page();
@@ -406,8 +510,12 @@ void attn_bf16_kernel(AttnArgs a) {
   auto pass = [&](const int t, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     // tile t+1 has landed once at most tiles t+2 .. t+DEPTH-1 are outstanding;
-    // the barrier makes every thread's loads and tile t's P^T visible
-    wait_vmcnt<(DEPTH - 2) * DMA_PER_THREAD>();
+    // the barrier makes every thread's loads and tile t's P^T visible (FP8:
+    // tile t+2's staged codes, decoded in this pass, and tile t+1's bf16 stage)
+    if constexpr (FP8)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<(DEPTH - 2) * DMA_PER_THREAD>();
     __syncthreads();
     // tile t+3 (possibly empty) goes to the stage that held tile t-1, read by
     // the previous pass; its loads are spread over this pass's PV MFMAs (all
@@ -418,14 +526,20 @@ void attn_bf16_kernel(AttnArgs a) {
     // latency is hidden behind the QK phase
     uint32_t flags;
     __builtin_memcpy(&flags, flag_xchg, 4);
-    const unsigned char* Kc = smem + (t % NSTAGE) * STAGE;
+    const unsigned char* Kc = smem + (t % NST) * STAGE;
     const int kb_next = k0 + (t + 1) * TILE;
     if constexpr (HAS_NEXT) {
-      const unsigned char* Kn = smem + ((t + 1) % NSTAGE) * STAGE;
+      const unsigned char* Kn = smem + ((t + 1) % NST) * STAGE;
       qk_begin(Kn);
 #pragma unroll
       for (int j = 0; j < 36; ++j) {
         qk_step(Kn, j, s_nx);
+        // FP8: tile t+3's codes into the staging slot tile t+1 left (decoded
+        // in the previous pass), one load after every seventh MFMA
+        if constexpr (FP8) {
+          if (j == 0) scl_nx = scale_of(nd);
+          if (j % 7 == 3 && j / 7 < F_DMA) dma16(nd.r, nd.dst + (j / 7) * 4096, dma_off[j / 7]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -484,12 +598,26 @@ void attn_bf16_kernel(AttnArgs a) {
           if constexpr (HAS_NEXT) {
             if (mi < SM_SLOTS) sm_slot(mi, s_nx, kb_next, false);
           }
-          // one of tile t+3's loads after every third MFMA
-          if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD) dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
+          if constexpr (FP8) {
+            // decode tile t+2 (staged in the previous pass) into the stage
+            // tile t-1 left: chunk c read after MFMA 7c, its halves after
+            // 7c+3 and 7c+5; the k^R chunk read after 28, stored after 30
+            unsigned char* S = smem + ((t + 2) % F_NSTAGE) * STAGE;
+            const unsigned char* F = smem + F_NSTAGE * STAGE + (t % F_NSLOT) * F_STAGE;
+            if (mi < 28 && mi % 7 == 0) cv_step(mi / 7, F, S, scl_cv);
+            if (mi < 28 && mi % 7 == 3) cv_step(4 + 2 * (mi / 7), F, S, scl_cv);
+            if (mi < 28 && mi % 7 == 5) cv_step(5 + 2 * (mi / 7), F, S, scl_cv);
+            if (mi == 28) cv_step(12, F, S, scl_cv);
+            if (mi == 30) cv_step(13, F, S, scl_cv);
+          } else {
+            // one of tile t+3's loads after every third MFMA
+            if (mi % 3 == 1 && mi / 3 < DMA_PER_THREAD) dma16(nd.r, nd.dst + (mi / 3) * 4096, dma_off[mi / 3]);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
+    if constexpr (FP8) scl_cv = scl_nx;
     // every wave is done with tile t's P^T and rescale slots
     __syncthreads();
     if constexpr (HAS_NEXT) publish();
@@ -834,7 +962,10 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int n_hg = (a.H + WG_HEADS - 1) / WG_HEADS;
   const int64_t n = (int64_t)a.max_items * n_hg;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+  if (a.fp8)
+    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3((unsigned)n), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)n), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

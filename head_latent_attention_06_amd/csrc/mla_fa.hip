@@ -555,8 +555,24 @@ __global__ void gather_rows_kernel(GatherArgs g) {
   u32x4 v = {0u, 0u, 0u, 0u};
   const int page = pidx < g.max_pages ? g.block_table[(int64_t)b * g.max_pages + pidx] : -1;
   if (page >= 0 && (int64_t)page < g.num_pages) {
-    v = *reinterpret_cast<const u32x4*>((const bf16*)g.pool + ((int64_t)page * g.page_size + j % g.page_size) * g.row +
-                                        8 * c);
+    const int64_t slot = (int64_t)page * g.page_size + j % g.page_size;
+    if (g.fp8) {
+      // 656-byte rows: E4M3 codes of c^KV (scale 2^e per 128 values at byte
+      // 640 + 4 tile), then k^R in bf16 from byte 512
+      const unsigned char* r = (const unsigned char*)g.pool + slot * 656;
+      if (c < 64) {
+        const uint2 w = *reinterpret_cast<const uint2*>(r + 8 * c);
+        const float sc = *reinterpret_cast<const float*>(r + 640 + 4 * (c >> 4));
+        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, false));
+        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, true));
+        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, false));
+        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, true));
+      } else {
+        v = *reinterpret_cast<const u32x4*>(r + 512 + 16 * (c - 64));
+      }
+    } else {
+      v = *reinterpret_cast<const u32x4*>((const bf16*)g.pool + slot * g.row + 8 * c);
+    }
   } else if (c == 0 && g.err_flags) {
     atomicOr(g.err_flags, 1);
   }

@@ -25,7 +25,8 @@ struct AttnArgs {
   const void* q_lat;          // [n_rows, H, ld_q]: first d_c = W_i^UK^T q^C_i
   const void* q_rope;         // [n_rows, H, ld_r]: first d_rope = q^R_i (rotated)
   int32_t ld_q, ld_r;
-  const void* pool;           // [num_pages, page_size, d_c + d_rope]
+  const void* pool;           // [num_pages, page_size, d_c + d_rope] (fp8: 656-byte rows)
+  int32_t fp8;                // FP8 cache rows (bf16 kernel only)
   const int32_t* block_table; // [B, max_pages]
   int64_t num_pages;
   int32_t max_pages, page_size;
@@ -118,6 +119,7 @@ struct AppendArgs {
   float eps;
   RopeParams rope;
   int32_t bf16_cache;                // cache dtype is bf16 (else fp32)
+  int32_t fp8_cache;                 // FP8 rows (656 bytes; d_c = 512, d_rope = 64)
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
@@ -164,6 +166,7 @@ struct GatherArgs {
   const void* pool; int64_t num_pages;
   const int32_t* block_table; int32_t max_pages, page_size;
   int32_t B, kv_end, row;
+  int32_t fp8;                // FP8 cache rows, decoded to bf16 (row = 576)
   int32_t* err_flags;
   void* out;
 };

@@ -111,6 +111,94 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   }
 }
 
+// FP8 cache rows, 656 bytes: c^KV as 512 E4M3 codes, k^R as 64 bf16, then one
+// fp32 scale 2^e per 128-value tile of c^KV (the FP8 passage of the
+// hnwysp.cn digest quantises activations in 1 x 128 tiles, each with its own
+// scale; the power-of-two scale is this library's reading).  e is the
+// smallest integer with max |x| <= 448 * 2^e over the tile, and each code is
+// x * 2^-e (exact) rounded to the nearest E4M3 value, ties to even.
+// One wave per token; lane l holds dims 8l .. 8l+7, in tile l / 16.
+constexpr int FP8_ROW = 656, FP8_KR = 512, FP8_SCALE = 640;
+template <typename TIN>
+__global__ __launch_bounds__(64) void append_fp8_kernel(AppendArgs a) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  int b, pos;
+  if (a.seq_idx) {
+    b = a.seq_idx[i];
+    pos = a.pos[i];
+  } else {
+    b = i / a.L;
+    pos = a.start_pos + i % a.L;
+  }
+  if (b < 0 || b >= a.n_seqs) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_SEQ);
+    return;
+  }
+  const int pidx = pos >= 0 ? pos / a.page_size : -1;
+  if (pidx < 0 || pidx >= a.max_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_POS);
+    return;
+  }
+  const int page = a.block_table[(int64_t)b * a.max_pages + pidx];
+  if (page < 0 || (int64_t)page >= a.num_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
+    return;
+  }
+  unsigned char* dst = (unsigned char*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * FP8_ROW;
+  const int64_t ci = (int64_t)i * a.ld_ckv, ki = (int64_t)i * a.ld_kr;
+  const auto in = [&](const void* p, int64_t o) {
+    float x = ld_as_f32<TIN>(p, o);
+    if (a.part_stride) x += ld_as_f32<TIN>(p, o + a.part_stride);
+    return x;
+  };
+  // RMSNorm of the latent (d_c = 512)
+  float y[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    y[k] = in(a.ckv, ci + 8 * lane + k);
+    ss += y[k] * y[k];
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / 512.f + a.eps);
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    y[k] = y[k] * inv * ld_as_f32<bf16>(a.g_kv, 8 * lane + k);
+    amax = fmaxf(amax, fabsf(y[k]));
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // amax = m 2^x, m in [0.5, 1), and 448 = 0.875 * 2^9
+  int x2;
+  const float m = frexpf(amax, &x2);
+  const int e = amax > 0.f ? (m <= 0.875f ? x2 - 9 : x2 - 8) : 0;
+  const float down = ldexpf(1.f, -e);
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h] * down, y[4 * h + 1] * down, 0, false);
+    w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2] * down, y[4 * h + 3] * down, (int)v, true);
+  }
+  *reinterpret_cast<uint2*>(dst + 8 * lane) = make_uint2(w[0], w[1]);
+  if ((lane & 15) == 0) *reinterpret_cast<float*>(dst + FP8_SCALE + 4 * (lane >> 4)) = ldexpf(1.f, e);
+  // RoPE of the shared decoupled key (d_rope = 64), bf16
+  if (lane < 32) {
+    const int p = lane;
+    float c, s;
+    if (a.rope_cs) {
+      const float* cs = a.rope_cs + ((int64_t)(i % a.L) * 32 + p) * 2;
+      c = cs[0];
+      s = cs[1];
+    } else {
+      rope_cos_sin(pos, p, 64, a.rope, c, s);
+    }
+    const float x0 = in(a.kr, ki + 2 * p), x1 = in(a.kr, ki + 2 * p + 1);
+    *reinterpret_cast<uint32_t*>(dst + FP8_KR + 4 * p) = pack_bf16x2(c * x0 - s * x1, s * x0 + c * x1);
+  }
+}
+
 __global__ void rope_table_kernel(float* out, int L, int start_pos, int d_rope, RopeParams rp) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = d_rope / 2;
@@ -160,7 +248,12 @@ unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per)
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   dim3 grid((unsigned)a.n), block(64);
-  if (a.bf16_cache) {
+  if (a.fp8_cache) {  // bf16 compute, d_c = 512, d_rope = 64 (checked by the caller)
+    if (a.in_f32)
+      hipLaunchKernelGGL((append_fp8_kernel<float>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((append_fp8_kernel<bf16>), grid, block, 0, st, a);
+  } else if (a.bf16_cache) {
     if (a.in_f32)
       hipLaunchKernelGGL((append_kernel<float, bf16>), grid, block, 0, st, a);
     else

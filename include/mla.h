@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum {
   MLA_OK = 0,
@@ -99,6 +99,14 @@ typedef struct {
   float yarn_alpha;
   float yarn_beta;
   int32_t yarn_orig_ctx;
+  /* FP8 latent cache (0 or 1; MLA_BF16 only).  The hnwysp.cn digest's FP8
+   * passage (DeepSeek-V3's fine-grained quantisation) scales activations per
+   * 1 x 128 tile; the cache applies that to c^KV: E4M3 codes (OCP "e4m3fn",
+   * largest finite 448) with one power-of-two scale 2^e per 128 values, e the
+   * smallest integer with max|x| <= 448 * 2^e, codes rounded to nearest, ties
+   * to even.  k^R stays bf16.  Attention still computes in bf16 with fp32
+   * accumulation on the decoded values.  See mla_kv_cache for the row. */
+  int32_t kv_fp8;
 } mla_config;
 
 /* Paged latent cache (host struct holding device pointers).
@@ -106,6 +114,11 @@ typedef struct {
  *              of sequence b lives at pool[block_table[b*max_pages_per_seq
  *              + p/page_size]][p % page_size]; its row is c^KV (RMSNorm'd,
  *              d_c values) followed by k^R (rotated, d_rope values).
+ *              With cfg->kv_fp8 a row is 656 bytes: bytes 0..511 the E4M3
+ *              codes of c^KV, 512..639 k^R as 64 bf16, 640..655 four fp32
+ *              scales 2^e (scale t covers c^KV values 128t .. 128t+127);
+ *              value d of c^KV is code(d) * scale(d / 128).
+ *              mla_cache_row_bytes() gives the row size for a config.
  *  block_table [n_seqs, max_pages_per_seq] int32 page ids.
  *  err_flags   optional int32 word (may be NULL).  Kernels that meet a page
  *              id outside [0, num_pages), a position beyond the table, or a
@@ -136,6 +149,11 @@ typedef struct {
 
 /* Version of this interface (MLA_ABI_VERSION). */
 int32_t mla_abi_version(void);
+
+/* Bytes of one cached row for cfg (host): (d_c + d_rope) elements of
+ * cfg->dtype, or 656 with kv_fp8; -1 if cfg fails the checks every entry
+ * point makes (see mla_status). */
+int64_t mla_cache_row_bytes(const mla_config* cfg);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status status);

@@ -305,20 +305,24 @@ def decode(rows_per_seq, kv_lens, s_q: int, q_nope, q_pe, w_uk, w_uv, d_c: int, 
 
 
 def prefill(h, w, n_heads: int, eps: float, base: float, scale: float, start_pos: int = 0,
-            past_rows=None, tokens=None, heads=None, yarn=None):
+            past_rows=None, tokens=None, heads=None, yarn=None, kv_fp8: bool = False):
     """Steps (1)-(10) for one sequence: h [L, d] holds tokens start_pos .. start_pos+L-1.
 
     ``past_rows`` [start_pos, d_c + d_rope] are the rows already cached for
     earlier positions.  Returns (o [len(tokens), len(heads), d_h], new_rows
     [L, d_c + d_rope]).  ``tokens`` selects which new tokens' outputs to compute.
     With ``yarn`` the RoPE frequencies are YaRN's and the logits are scaled by
-    yarn_logit_factor(s) on top of ``scale``.
+    yarn_logit_factor(s) on top of ``scale``.  With ``kv_fp8`` the cache holds
+    c^KV in the FP8 format (quantize_latent_fp8) and attention reads those
+    values; new_rows are then the dequantised rows.
     """
     h = _f64(h)
     L = h.shape[0]
     pos = start_pos + np.arange(L)
     d_c = np.asarray(w["w_dkv"]).shape[0]
     c, k_r = latent_rows(h, w["w_dkv"], w["g_kv"], w["w_kr"], pos, eps, base, yarn)
+    if kv_fp8:
+        c = quantize_latent_fp8(c)[2]
     new_rows = np.concatenate([c, k_r], axis=1)
     rows = new_rows if past_rows is None or start_pos == 0 else np.concatenate([_f64(past_rows), new_rows])
     tokens = np.arange(L) if tokens is None else np.asarray(tokens)

@@ -145,3 +145,20 @@ def test_output_projection_workspace(lib):
     # a call with a misaligned pointer is refused before any launch
     assert lib.mla_output_projection(ctypes.byref(_cfg()), FAKE + 2, 16384, FAKE, FAKE, 64, FAKE, 1 << 30,
                                      None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_fp8_cache_config(lib):
+    """kv_fp8: 656-byte rows (512 codes, 64 bf16 of k^R, four fp32 scales),
+    bf16 compute only, the flag itself 0 or 1."""
+    import torch
+    n = ctypes.c_size_t()
+    assert lib.mla_cache_row_bytes(ctypes.byref(_cfg())) == 1152
+    assert lib.mla_cache_row_bytes(ctypes.byref(_cfg(kv_fp8=True))) == 656
+    assert lib.mla_cache_row_bytes(ctypes.byref(_cfg(d_c=64, d_rope=8, dtype=torch.float32))) == 72 * 4
+    assert lib.mla_cache_row_bytes(ctypes.byref(_cfg(d_c=256))) == -1
+    assert lib.mla_decode_workspace_size(ctypes.byref(_cfg(kv_fp8=True)), 4, 1, 4097, ctypes.byref(n)) == mla.MLA_OK
+    c = _cfg(kv_fp8=True, dtype=torch.float32, d_c=64, d_rope=8)
+    assert lib.mla_decode_workspace_size(ctypes.byref(c), 1, 1, 10, ctypes.byref(n)) == mla.MLA_ERR_UNSUPPORTED
+    bad = _cfg()
+    bad.kv_fp8 = 2
+    assert lib.mla_decode_workspace_size(ctypes.byref(bad), 1, 1, 10, ctypes.byref(n)) == mla.MLA_ERR_INVALID_ARG
