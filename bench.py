@@ -75,26 +75,37 @@ def _up(a, dtype=torch.bfloat16):
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(dtype)
 
 
-def decode_workload(copies: int):
+def decode_workload(copies: int, fp8: bool = False):
     inp = mi.decode_inputs(2, mi.V3, mi.config_context_lens(2), 1)
-    cfg = mla.Config(**CFG_EXTRA)
+    cfg = mla.Config(kv_fp8=fp8, **CFG_EXTRA)
     bt, npages = mi.block_table(2, inp.kv_lens, cfg.page_size, shuffle=True)
-    pool = torch.empty((npages, cfg.page_size, cfg.row), dtype=torch.bfloat16, device="cuda")
-    flat = pool.view(-1, cfg.row)
-    for b in range(len(inp.kv_lens)):
-        n = int(inp.kv_lens[b])
-        pos = np.arange(n)
-        idx = torch.from_numpy(bt[b, pos // cfg.page_size].astype(np.int64) * cfg.page_size + pos % cfg.page_size)
-        flat[idx.cuda()] = _up(inp.seq_rows(b))
     btd = torch.from_numpy(bt).cuda()
+    if fp8:
+        # the FP8 rows are written by the library's append, from the drawn rows
+        # taken as raw c^KV and k^R (unit RMSNorm gains)
+        pool = torch.empty((npages, cfg.page_size, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+        rows = _up(inp.rows)
+        seq = np.repeat(np.arange(len(inp.kv_lens)), inp.kv_lens).astype(np.int32)
+        pos = np.concatenate([np.arange(n) for n in inp.kv_lens]).astype(np.int32)
+        mla.mla_cache_append(cfg, mla.PagedCache(pool, btd), rows[:, :cfg.d_c].contiguous(),
+                             rows[:, cfg.d_c:].contiguous(), torch.ones(cfg.d_c, dtype=torch.bfloat16, device="cuda"),
+                             torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda())
+    else:
+        pool = torch.empty((npages, cfg.page_size, cfg.row), dtype=torch.bfloat16, device="cuda")
+        flat = pool.view(-1, cfg.row)
+        for b in range(len(inp.kv_lens)):
+            n = int(inp.kv_lens[b])
+            pos = np.arange(n)
+            idx = torch.from_numpy(bt[b, pos // cfg.page_size].astype(np.int64) * cfg.page_size + pos % cfg.page_size)
+            flat[idx.cuda()] = _up(inp.seq_rows(b))
     caches = [mla.PagedCache(pool if i == 0 else pool.clone(), btd) for i in range(copies)]
     t = dict(q_nope=_up(inp.q_nope), q_pe=_up(inp.q_pe), w_uk=_up(inp.w_uk), w_uv=_up(inp.w_uv),
              kv_lens=torch.from_numpy(inp.kv_lens).cuda())
     return inp, cfg, caches, t
 
 
-def run_decode_bench(steps: int, warmup: int):
-    inp, cfg, caches, t = decode_workload(4)
+def run_decode_bench(steps: int, warmup: int, fp8: bool = False):
+    inp, cfg, caches, t = decode_workload(4, fp8)
     B, max_kv = len(inp.kv_lens), int(inp.kv_lens.max())
     out = torch.empty((B, 1, cfg.n_heads, cfg.d_head), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mla.mla_decode_workspace_size(cfg, B, 1, max_kv), dtype=torch.uint8, device="cuda")
@@ -119,10 +130,26 @@ def run_decode_bench(steps: int, warmup: int):
     torch.cuda.synchronize()
     attn_list = [ev.elapsed_ms(i) for i in range(steps)]
     ev.close()
-    latent_bytes = int(inp.kv_lens.sum()) * cfg.row * 2
+    latent_bytes = int(inp.kv_lens.sum()) * cfg.row_bytes
     flops = int(inp.kv_lens.sum()) * cfg.n_heads * (cfg.row + cfg.d_c) * 2
     return dict(inp=inp, wall=wall, attn_ms=float(np.mean(attn_list)), attn_list=attn_list,
                 latent_bytes=latent_bytes, attn_flops=flops)
+
+
+def run_fp8_summary(steps: int, warmup: int, bf16_attn_ms: float) -> dict:
+    """The decode workload over an FP8 latent cache (656-byte rows)."""
+    d = run_decode_bench(steps, warmup, fp8=True)
+    ms = d["wall"] / steps * 1e3
+    gbs = d["latent_bytes"] / (d["attn_ms"] * 1e-3) / 1e9
+    return {"workload": "MLA decode step over an FP8 latent cache (E4M3 c^KV, 1x128 power-of-two scales, bf16 "
+                        "k^R: 656 B/token), B=64 x 4097 tokens, n_h=128, 64-token pages",
+            "ms_per_step": round(ms, 4), "cache_bytes": d["latent_bytes"],
+            "cache_gbs_step": round(d["latent_bytes"] / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "kernel": "attn_bf16_kernel<fp8>", "kernel_ms": round(d["attn_ms"], 5),
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
+            "attn_time_vs_bf16_cache": round(d["attn_ms"] / bf16_attn_ms, 3)}
 
 
 def prefill_flops(s: mi.Shape, L: int, explicit: bool) -> dict:
@@ -410,6 +437,7 @@ def main():
                      "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
     }
     res["output_projection"] = run_output_projection_bench(args.steps, args.warmup)
+    res["fp8_cache"] = run_fp8_summary(max(20, args.steps // 2), max(20, args.warmup // 4), d["attn_ms"])
     if args.other_decode:
         res["other_decode"] = run_other_decode(max(10, args.steps // 4), max(20, args.warmup // 4))
     if not args.no_prefill:

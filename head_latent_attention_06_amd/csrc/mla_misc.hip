@@ -112,9 +112,9 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 }
 
 // FP8 cache rows, 656 bytes: c^KV as 512 E4M3 codes, k^R as 64 bf16, then one
-// fp32 scale 2^e per 128-value tile of c^KV (the FP8 passage of the
-// hnwysp.cn digest quantises activations in 1 x 128 tiles, each with its own
-// scale; the power-of-two scale is this library's reading).  e is the
+// fp32 scale 2^e per 128-value tile of c^KV (the notes page, section 二(三)
+// "FP8训练", quantises activations in 1 x 128 tiles, each with its own scale;
+// the power-of-two scale is this library's reading).  e is the
 // smallest integer with max |x| <= 448 * 2^e over the tile, and each code is
 // x * 2^-e (exact) rounded to the nearest E4M3 value, ties to even.
 // One wave per token; lane l holds dims 8l .. 8l+7, in tile l / 16.

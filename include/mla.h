@@ -99,8 +99,8 @@ typedef struct {
   float yarn_alpha;
   float yarn_beta;
   int32_t yarn_orig_ctx;
-  /* FP8 latent cache (0 or 1; MLA_BF16 only).  The hnwysp.cn digest's FP8
-   * passage (DeepSeek-V3's fine-grained quantisation) scales activations per
+  /* FP8 latent cache (0 or 1; MLA_BF16 only).  The notes page, section
+   * 二(三) "FP8训练" (fine-grained quantisation), scales activations per
    * 1 x 128 tile; the cache applies that to c^KV: E4M3 codes (OCP "e4m3fn",
    * largest finite 448) with one power-of-two scale 2^e per 128 values, e the
    * smallest integer with max|x| <= 448 * 2^e, codes rounded to nearest, ties

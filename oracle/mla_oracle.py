@@ -46,9 +46,9 @@ design notes of the repository):
   * Decode: the step's s_q new tokens are already cached; query s of a
     sequence with kv_len cached rows sits at position kv_len - s_q + s and
     attends to rows j <= that position.
-  * FP8 latent cache (optional; the hnwysp.cn digest's FP8 passage fixes only
-    the granularity: activations are quantised per 1 x 128 tile, each tile
-    with its own scale).  The format is OCP E4M3 ("e4m3fn": 4 exponent bits,
+  * FP8 latent cache (optional; the notes page, section 二(三) "FP8训练",
+    fixes only the granularity: activations are quantised per 1 x 128 tile,
+    each tile with its own scale, and products accumulate in FP32).  The format is OCP E4M3 ("e4m3fn": 4 exponent bits,
     bias 7, 3 mantissa bits, largest finite 448, no infinities).  Each
     128-value tile of c^KV gets a power-of-two scale 2^e, e the smallest
     integer with max|x| <= 448 * 2^e, and codes round x / 2^e to the nearest
