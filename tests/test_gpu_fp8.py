@@ -113,7 +113,7 @@ def test_fp8_append_codes_scales_and_rope():
     assert np.all(pool[last, n % shape.page_size:] == 0xFF)
 
 
-def _decode_case(seed, contexts, s_q, page_size, heads=None, seqs_check=None):
+def _decode_case(seed, contexts, s_q, page_size, heads=None):
     shape = _shape(page_size)
     cfg = _cfg(shape)
     inp = mi.decode_inputs(seed, shape, contexts, s_q)
@@ -227,3 +227,33 @@ def test_fp8_prefill_8192_sampled(form):
     print(f"rel_l2={err:.3e} rows={rerr:.3e}")
     assert err <= BF16_TOL
     assert rerr <= BF16_TOL
+
+
+def test_fp8_decode_bench_workload_sampled():
+    """The timed FP8 decode workload: B=64 sequences x 4097 tokens, s_q=1,
+    64-token shuffled pages, the full step (all 64 x 128 outputs computed);
+    the oracle checks three sequences on three heads."""
+    seqs, heads = [0, 31, 63], [0, 77, 127]
+    shape = _shape(64)
+    cfg = _cfg(shape)
+    inp = mi.decode_inputs(2, shape, mi.config_context_lens(2), 1)
+    g = _gains(2)
+    bt, npages = mi.block_table(2, inp.kv_lens, 64, shuffle=True)
+    cache = _cache(cfg, npages, bt)
+    raws = [inp.seq_rows(b) for b in range(len(inp.kv_lens))]
+    print("[fp8 decode B=64 x 4097]", flush=True)
+    _append(cfg, cache, raws, g)
+    out = torch.empty((64, 1, shape.n_heads, shape.d_head), dtype=torch.bfloat16, device="cuda")
+    mla.mla_decode(cfg, cache, torch.from_numpy(inp.kv_lens).to("cuda"), int(inp.kv_lens.max()), dev(inp.q_nope),
+                   dev(inp.q_pe), dev(inp.w_uk), dev(inp.w_uv), out)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    got = host(out)
+    assert np.isfinite(got).all()
+    rows8 = [_oracle_rows(raws[b], g, shape)[3] if b in seqs else None for b in range(len(raws))]
+    ref = om.decode(rows8, inp.kv_lens, 1, inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, shape.d_c, shape.scale,
+                    seqs=seqs, heads=heads)
+    for k, b in enumerate(seqs):
+        err = rel_l2(got[b][:, heads], ref[k])
+        print(f"b={b} rel_l2={err:.3e}")
+        assert err <= BF16_TOL
