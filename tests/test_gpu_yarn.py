@@ -108,3 +108,30 @@ def test_yarn_decode_logit_factor():
     print(f"yarn decode rel_l2={err:.3e}")
     assert err <= BF16_TOL
     assert rel_l2(oracle_decode(inp), ref) > 5 * BF16_TOL
+
+
+@pytest.mark.parametrize("form", [pytest.param(mla.PREFILL_ABSORBED, id="absorbed"),
+                                  pytest.param(mla.PREFILL_EXPLICIT, id="explicit")])
+def test_yarn_prefill_v3_fp8_cache(form):
+    """YaRN with the FP8 latent cache: the FP8 append rotates k^R with YaRN's
+    frequencies (kept in bf16) and both attention forms read the FP8 rows."""
+    s = mi.V3
+    cfg = _yarn_cfg(s, torch.bfloat16, form)
+    cfg.kv_fp8 = True
+    L = 300
+    w = mi.weights(63, s)
+    h = mi.hidden(63, s, 1, L)
+    bt, npages = mi.block_table(63, [L], s.page_size, shuffle=True)
+    pool = torch.full((npages, s.page_size, cfg.row_bytes), 0xFF, dtype=torch.uint8, device="cuda")
+    cache = mla.PagedCache(pool, torch.from_numpy(bt).cuda(), torch.zeros(1, dtype=torch.int32, device="cuda"))
+    out = torch.empty((1, L, s.n_heads, s.d_head), dtype=torch.bfloat16, device="cuda")
+    mla.mla_prefill(cfg, cache, {k: dev(v) for k, v in w.items()}, dev(h), out)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    ref, rows = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, yarn=YARN, kv_fp8=True)
+    err = rel_l2(host(out)[0], ref)
+    p = om.paged_gather(pool.cpu().numpy(), bt, 0, L, s.page_size)
+    kr = (p[:, 512:640].copy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    print(f"rel_l2={err:.3e} k^R rel_l2={rel_l2(kr, rows[:, 512:]):.3e}", flush=True)
+    assert err <= BF16_TOL
+    assert rel_l2(kr, rows[:, 512:]) <= BF16_TOL
