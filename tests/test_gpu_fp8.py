@@ -257,3 +257,72 @@ def test_fp8_decode_bench_workload_sampled():
         err = rel_l2(got[b][:, heads], ref[k])
         print(f"b={b} rel_l2={err:.3e}")
         assert err <= BF16_TOL
+
+
+def test_fp8_decode_bad_page_and_length_are_flagged():
+    """With an FP8 cache, a block-table entry outside the pool and a length
+    past the bound are reported in err_flags and skipped; the valid row is
+    unaffected and the invalid one is written as zeros."""
+    shape = _shape(64)
+    cfg = _cfg(shape)
+    inp = mi.decode_inputs(115, shape, [100, 100], 1)
+    g = _gains(115)
+    bt, npages = mi.block_table(115, inp.kv_lens, 64, shuffle=True)
+    cache = _cache(cfg, npages, bt)
+    raws = [inp.seq_rows(b) for b in range(2)]
+    _append(cfg, cache, raws, g)
+    out = torch.empty((2, 1, shape.n_heads, shape.d_head), dtype=torch.bfloat16, device="cuda")
+    args = (dev(inp.q_nope), dev(inp.q_pe), dev(inp.w_uk), dev(inp.w_uv), out)
+    bad = cache.block_table.clone()
+    bad[0, 1] = npages + 5  # page id past the pool
+    mla.mla_decode(cfg, mla.PagedCache(cache.pool, bad, cache.err_flags),
+                   torch.from_numpy(inp.kv_lens).to("cuda"), 101, *args)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) & mla.MLA_FLAG_BAD_PAGE
+    cache.err_flags.zero_()
+    mla.mla_decode(cfg, cache, torch.tensor([101, 500], dtype=torch.int32, device="cuda"), 101, *args)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) & mla.MLA_FLAG_BAD_LEN
+    assert torch.all(out[1].float() == 0)
+    ref = om.decode([_oracle_rows(raws[0], g, shape)[3]], inp.kv_lens[:1], 1, inp.q_nope[:1], inp.q_pe[:1],
+                    inp.w_uk, inp.w_uv, shape.d_c, shape.scale)
+    assert rel_l2(host(out)[0:1], ref) <= BF16_TOL
+
+
+def test_fp8_decode_hip_graph_replay_matches_eager():
+    """The FP8 decode step captured in a HIP graph replays bit-identically to
+    eager launches, with eager work between replays."""
+    shape = _shape(64)
+    cfg = _cfg(shape)
+    inp = mi.decode_inputs(116, shape, [40, 300, 1000, 2047], 1)
+    bt, npages = mi.block_table(116, inp.kv_lens, 64, shuffle=True)
+    cache = _cache(cfg, npages, bt)
+    _append(cfg, cache, [inp.seq_rows(b) for b in range(4)], _gains(116))
+    max_kv = int(inp.kv_lens.max())
+    out = torch.empty((4, 1, shape.n_heads, shape.d_head), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_size(cfg, 4, 1, max_kv), dtype=torch.uint8, device="cuda")
+    t = [torch.from_numpy(inp.kv_lens).to("cuda"), dev(inp.q_nope), dev(inp.q_pe), dev(inp.w_uk), dev(inp.w_uv)]
+
+    def step():
+        mla.mla_decode(cfg, cache, t[0], max_kv, t[1], t[2], t[3], t[4], out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
