@@ -326,3 +326,28 @@ def test_fp8_decode_hip_graph_replay_matches_eager():
         assert torch.equal(out, eager), f"replay {i} differs"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("L", [10752, 10753])
+def test_fp8_project_kv_both_sides_of_the_k_split(L):
+    """[W^DKV ; W^KR] h then the FP8 append, at the last token count whose
+    projection runs as two k-halves summed by the append (10752) and the first
+    that runs as one (10753); sampled rows against the oracle's FP8 rows."""
+    shape = S
+    cfg = _cfg(shape)
+    w = mi.weights(117, shape)
+    h = mi.hidden(117 + L, shape, 1, L)
+    bt, npages = mi.block_table(117, [L], shape.page_size, shuffle=True)
+    cache = _cache(cfg, npages, bt)
+    print(f"[fp8 project_kv] L={L}", flush=True)
+    mla.mla_project_kv(cfg, cache, {k: dev(w[k]) for k in ("w_dkv", "w_kr", "g_kv")}, dev(h))
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    pool = cache.pool.cpu().numpy()
+    toks = np.unique(np.array([0, 1, 255, 256, 4095, L // 2, L - 257, L - 256, L - 2, L - 1]))
+    c, kr = om.latent_rows(h[0][toks], w["w_dkv"], w["g_kv"], w["w_kr"], toks, shape.rms_eps, shape.rope_base)
+    ref = np.concatenate([om.quantize_latent_fp8(c)[2], kr], axis=1)
+    got = _deq(np.stack([pool[om.paged_slot(bt, 0, int(t), shape.page_size)] for t in toks]))
+    err = rel_l2(got, ref)
+    print(f"rows rel_l2={err:.3e}")
+    assert err <= BF16_TOL
