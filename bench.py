@@ -404,8 +404,8 @@ def main():
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
-              "build: sequences shard across GPUs with no exchange (see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): decode sequences shard across GPUs "
+              "with no exchange, so N GPUs run N independent copies of this step", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

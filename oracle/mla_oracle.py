@@ -22,8 +22,7 @@ definition written out: it materialises every head's k and v and applies the
 max-subtracted softmax, all in float64.  The absorbed form (used only by the
 pins, to show the two forms agree) is a separate function.
 
-Readings where the pages leave a step open (each listed with its reason in the
-design notes of the repository):
+Readings where the pages leave a step open:
   * RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, applied to both c^KV and c^Q;
     k^R is not normalised (it is taken from h, not from a latent).
   * RoPE: rotation of adjacent pairs (x_2p, x_2p+1) by the 2x2 block
