@@ -1,0 +1,83 @@
+"""Head counts other than 128 (any multiple of 32 is served): one workgroup
+covers 128 heads, so 32 and 96 heads leave waves without heads and 160 heads
+take a second, partly filled head group.  Decode (bf16 and FP8 caches) and
+prefill (both forms) against the float64 oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_06_amd as mla
+import mla_inputs as mi
+from mla_testutil import BF16_TOL, config, decode_setup, dev, host, oracle_decode, paged_cache, rel_l2, run_decode
+from oracle import mla_oracle as om
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("H", [32, 96, 160])
+def test_decode_head_counts_bf16(H):
+    s = dataclasses.replace(mi.V3, n_heads=H)
+    print(f"[decode heads] H={H}", flush=True)
+    inp = mi.decode_inputs(121, s, [5, 300, 2047], 1)
+    cfg, cache, bt, t = decode_setup(inp, config_id=121)
+    out = run_decode(cfg, cache, t, int(inp.kv_lens.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    got, ref = host(out), oracle_decode(inp)
+    for b in range(3):
+        assert rel_l2(got[b], ref[b]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("H", [32, 160])
+def test_decode_head_counts_fp8(H):
+    s = dataclasses.replace(mi.V3, n_heads=H)
+    print(f"[decode heads fp8] H={H}", flush=True)
+    cfg = config(s)
+    cfg.kv_fp8 = True
+    inp = mi.decode_inputs(122, s, [5, 300, 2047], 1)
+    bt, npages = mi.block_table(122, inp.kv_lens, s.page_size, shuffle=True)
+    pool = torch.full((npages, s.page_size, cfg.row_bytes), 0xFF, dtype=torch.uint8, device="cuda")
+    cache = mla.PagedCache(pool, torch.from_numpy(bt).cuda(), torch.zeros(1, dtype=torch.int32, device="cuda"))
+    raws = [inp.seq_rows(b) for b in range(3)]
+    g = np.ones(s.d_c, np.float32)
+    ckv = np.concatenate([r[:, :s.d_c] for r in raws])
+    kr = np.concatenate([r[:, s.d_c:] for r in raws])
+    seq = np.concatenate([np.full(len(r), b, np.int32) for b, r in enumerate(raws)])
+    pos = np.concatenate([np.arange(len(r), dtype=np.int32) for r in raws])
+    mla.mla_cache_append(cfg, cache, dev(ckv), dev(kr), dev(g), torch.from_numpy(seq).cuda(),
+                         torch.from_numpy(pos).cuda())
+    out = torch.empty((3, 1, H, s.d_head), dtype=torch.bfloat16, device="cuda")
+    mla.mla_decode(cfg, cache, torch.from_numpy(inp.kv_lens).cuda(), int(inp.kv_lens.max()), dev(inp.q_nope),
+                   dev(inp.q_pe), dev(inp.w_uk), dev(inp.w_uv), out)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    rows = [om.cache_row_fp8(r[:, :s.d_c], r[:, s.d_c:], g, np.arange(len(r)), s.rms_eps, s.rope_base)[3]
+            for r in raws]
+    ref = om.decode(rows, inp.kv_lens, 1, inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, s.d_c, s.scale)
+    got = host(out)
+    for b in range(3):
+        assert rel_l2(got[b], ref[b]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("form", [pytest.param(mla.PREFILL_ABSORBED, id="absorbed"),
+                                  pytest.param(mla.PREFILL_EXPLICIT, id="explicit")])
+def test_prefill_96_heads(form):
+    s = dataclasses.replace(mi.V3, n_heads=96)
+    print(f"[prefill heads] H=96 form={form}", flush=True)
+    cfg = config(s)
+    cfg.prefill_form = form
+    L = 130
+    w = mi.weights(123, s)
+    h = mi.hidden(123, s, 1, L)
+    bt, npages = mi.block_table(123, [L], s.page_size, shuffle=True)
+    cache = paged_cache(cfg, npages, bt)
+    out = torch.empty((1, L, 96, s.d_head), dtype=torch.bfloat16, device="cuda")
+    mla.mla_prefill(cfg, cache, {k: dev(v) for k, v in w.items()}, dev(h), out)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    ref, _ = om.prefill(h[0], w, 96, s.rms_eps, s.rope_base, s.scale)
+    err = rel_l2(host(out)[0], ref)
+    print(f"rel_l2={err:.3e}")
+    assert err <= BF16_TOL
