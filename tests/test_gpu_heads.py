@@ -1,7 +1,9 @@
 """Head counts other than 128 (any multiple of 32 is served): one workgroup
 covers 128 heads, so 32 and 96 heads leave waves without heads and 160 heads
-take a second, partly filled head group.  Decode (bf16 and FP8 caches) and
-prefill (both forms) against the float64 oracle."""
+take a second, partly filled head group.  Head widths d_h = 64 and 256 (any
+multiple of 64 up to 512 is served) take the separate merge and W^UV GEMM in
+decode and the absorbed form in prefill.  Decode (bf16 and FP8 caches) and
+prefill against the float64 oracle."""
 import dataclasses
 
 import numpy as np
@@ -79,5 +81,52 @@ def test_prefill_96_heads(form):
     assert int(cache.err_flags.item()) == 0
     ref, _ = om.prefill(h[0], w, 96, s.rms_eps, s.rope_base, s.scale)
     err = rel_l2(host(out)[0], ref)
+    print(f"rel_l2={err:.3e}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("dh", [64, 256])
+def test_decode_head_widths(dh):
+    """d_h = 64 and 256: the absorption GEMM with K = d_h and, since the fused
+    merge + W^UV kernel is written for d_h = 128, the separate merge followed
+    by the batched W^UV GEMM."""
+    s = dataclasses.replace(mi.V3, d_head=dh)
+    print(f"[decode d_h] {dh}", flush=True)
+    inp = mi.decode_inputs(124, s, [5, 300, 2047], 2)
+    cfg, cache, bt, t = decode_setup(inp, config_id=124)
+    out = run_decode(cfg, cache, t, int(inp.kv_lens.max()))
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    got, ref = host(out), oracle_decode(inp)
+    for b in range(3):
+        err = rel_l2(got[b], ref[b])
+        print(f"b={b} rel_l2={err:.3e}")
+        assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("dh", [64, 256])
+def test_prefill_head_widths_absorbed(dh):
+    """Prefill at d_h = 64 and 256 (the absorbed form; the explicit form is
+    built for d_h = 128 and is refused for other widths)."""
+    s = dataclasses.replace(mi.V3, d_head=dh)
+    print(f"[prefill d_h] {dh}", flush=True)
+    cfg = config(s)
+    L = 200
+    w = mi.weights(125, s)
+    h = mi.hidden(125, s, 1, L)
+    bt, npages = mi.block_table(125, [L], s.page_size, shuffle=True)
+    cache = paged_cache(cfg, npages, bt)
+    out = torch.empty((1, L, s.n_heads, dh), dtype=torch.bfloat16, device="cuda")
+    wd = {k: dev(v) for k, v in w.items()}
+    cfg.prefill_form = mla.PREFILL_EXPLICIT
+    with pytest.raises(mla.MLAError):
+        mla.mla_prefill(cfg, cache, wd, dev(h), out)
+    cfg.prefill_form = mla.PREFILL_AUTO
+    mla.mla_prefill(cfg, cache, wd, dev(h), out)
+    torch.cuda.synchronize()
+    assert int(cache.err_flags.item()) == 0
+    toks = np.array([0, 1, 63, 64, 127, 199])
+    ref, _ = om.prefill(h[0], w, s.n_heads, s.rms_eps, s.rope_base, s.scale, tokens=toks, heads=[0, 77, 127])
+    err = rel_l2(host(out)[0][toks][:, [0, 77, 127]], ref)
     print(f"rel_l2={err:.3e}")
     assert err <= BF16_TOL
