@@ -1,11 +1,13 @@
-"""Shapes beside the DeepSeek-V3 defaults.  Head counts other than 128 (any
-multiple of 32 is served): one workgroup
-covers 128 heads, so 32 and 96 heads leave waves without heads and 160 heads
-take a second, partly filled head group.  Head widths d_h = 64 and 256 (any
-multiple of 64 up to 512 is served) take the separate merge and W^UV GEMM in
-decode and the absorbed form in prefill.  Pages of 96 (not a power of two)
-and 256 tokens.  Decode (bf16 and FP8 caches) and prefill against the
-float64 oracle."""
+"""Shapes beside the DeepSeek-V3 defaults, against the float64 oracle.
+
+* Head counts other than 128 (any multiple of 32 is served): one workgroup
+  covers 128 heads, so 32 and 96 heads leave waves without heads and 160
+  heads take a second, partly filled head group.
+* Head widths d_h = 64 and 256 (any multiple of 64 up to 512 is served): the
+  separate merge and W^UV GEMM in decode, the absorbed form in prefill.
+* Pages of 96 (not a power of two) and 256 tokens.
+
+Decode over bf16 and FP8 caches, prefill in both forms where served."""
 import dataclasses
 
 import numpy as np
