@@ -224,6 +224,40 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const float* x, int64_t ldx
   for (int d = lane; d < width; d += 64) out[r * ldo + d] = from_f32<TOUT>(xr[d] * inv * to_f32(((const TOUT*)g)[d]));
 }
 
+// The same for bf16 output and width a multiple of 256 (at most 2048): each
+// lane moves 4 consecutive values per access (16-byte loads of x, 8-byte
+// loads of g and stores), so a wave's access covers 1 KB of the row.
+constexpr int RMS4_MAX = 8;  // float4 groups per lane
+__global__ __launch_bounds__(64) void rmsnorm4_bf16_kernel(const float* x, int64_t ldx, const bf16* g, bf16* out,
+                                                           int64_t ldo, int width, float eps) {
+  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + r * ldx);
+  const int nv = width / 256;
+  float4 v[RMS4_MAX];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < RMS4_MAX; ++k) {
+    if (k < nv) {
+      v[k] = xr[lane + 64 * k];
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)width + eps);
+#pragma unroll
+  for (int k = 0; k < RMS4_MAX; ++k) {
+    if (k < nv) {
+      const int d = 4 * (lane + 64 * k);
+      const uint2 gw = *reinterpret_cast<const uint2*>(g + d);
+      const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xffff0000u);
+      const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xffff0000u);
+      *reinterpret_cast<uint2*>(out + r * ldo + d) =
+          make_uint2(pack_bf16x2(v[k].x * inv * g0, v[k].y * inv * g1), pack_bf16x2(v[k].z * inv * g2, v[k].w * inv * g3));
+    }
+  }
+}
+
 // One thread per rotated pair.
 template <typename TOUT>
 __global__ void rope_heads_kernel(const float* x, const float* cs, int table_rows, TOUT* out, int64_t ld_out,
@@ -306,7 +340,12 @@ hipError_t launch_sum_partials(const float* p, int32_t S, int64_t n, void* out, 
 hipError_t launch_rmsnorm(const float* x, int64_t ldx, const void* g, void* out, int64_t ldo, int32_t rows,
                           int32_t width, float eps, int32_t bf16_io, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (bf16_io)
+  const auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+  if (bf16_io && width % 256 == 0 && width <= 256 * RMS4_MAX && ldx % 4 == 0 && ldo % 4 == 0 && al(x, 16) &&
+      al(out, 8) && al(g, 8))
+    hipLaunchKernelGGL(rmsnorm4_bf16_kernel, dim3(rows), dim3(64), 0, st, x, ldx, (const bf16*)g, (bf16*)out, ldo,
+                       width, eps);
+  else if (bf16_io)
     hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(rows), dim3(64), 0, st, x, ldx, g, (bf16*)out, ldo, width, eps);
   else
     hipLaunchKernelGGL((rmsnorm_kernel<float>), dim3(rows), dim3(64), 0, st, x, ldx, g, (float*)out, ldo, width, eps);
