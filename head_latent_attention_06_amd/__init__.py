@@ -25,9 +25,9 @@ MLA_FLAG_BAD_PAGE, MLA_FLAG_BAD_POS, MLA_FLAG_BAD_LEN, MLA_FLAG_BAD_SEQ = 1, 2, 
 
 
 class MLAError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: str = ""):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)}")
+        super().__init__(f"{where}: {status_string(status)}" + (f" ({detail})" if detail else ""))
 
 
 class _Config(ctypes.Structure):
@@ -142,7 +142,9 @@ class Config:
 
 @dataclass
 class PagedCache:
-    """Caller-owned paged latent cache: pool [num_pages, page_size, d_c + d_rope]."""
+    """Caller-owned paged latent cache: pool [num_pages, page_size, d_c + d_rope]
+    (any element type whose row is Config.row_bytes bytes, e.g. uint8 [.., 656]
+    for the FP8 cache)."""
 
     pool: torch.Tensor
     block_table: torch.Tensor          # [n_seqs, max_pages] int32
@@ -151,6 +153,62 @@ class PagedCache:
     def _c(self) -> _Cache:
         return _Cache(self.pool.data_ptr(), self.pool.shape[0], self.block_table.data_ptr(),
                       self.block_table.shape[1], self.err_flags.data_ptr() if self.err_flags is not None else None)
+
+
+# ---------------------------------------------------------------------------
+# Argument checks, made before any call into the library (the library checks
+# sizes and pointers too, but it cannot see a tensor's shape, dtype or layout:
+# a pool of the wrong row width would make its kernels address past it).
+def _bad(where: str, detail: str):
+    raise MLAError(MLA_ERR_INVALID_ARG, where, detail)
+
+
+def _tensor(where: str, name: str, t, dtype=None, shape=None) -> None:
+    """t is a contiguous tensor of dtype with the given shape (None = any extent);
+    where it lives is checked by _on_gpu once every shape has been."""
+    if not isinstance(t, torch.Tensor):
+        _bad(where, f"{name} is not a tensor")
+    if dtype is not None and t.dtype != dtype:
+        _bad(where, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(want is not None and got != want for got, want in zip(t.shape, shape))):
+        _bad(where, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        _bad(where, f"{name} is not contiguous")
+
+
+def _on_gpu(where: str, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            _bad(where, f"{name} is on {t.device}, expected a GPU tensor")
+
+
+def _cache_ok(where: str, cfg: "Config", cache: PagedCache, n_seqs: int) -> None:
+    p = cache.pool
+    if not isinstance(p, torch.Tensor) or p.dim() != 3:
+        _bad(where, "pool must be [num_pages, page_size, row]")
+    if p.shape[1] != cfg.page_size:
+        _bad(where, f"pool pages hold {p.shape[1]} tokens, the config says {cfg.page_size}")
+    if p.shape[2] * p.element_size() != cfg.row_bytes:
+        _bad(where, f"pool rows are {p.shape[2] * p.element_size()} bytes, the config needs {cfg.row_bytes}")
+    _tensor(where, "pool", p)
+    _tensor(where, "block_table", cache.block_table, torch.int32, (None, None))
+    if cache.block_table.shape[0] < n_seqs:
+        _bad(where, f"block_table has {cache.block_table.shape[0]} rows for {n_seqs} sequences")
+    if cache.err_flags is not None:
+        _tensor(where, "err_flags", cache.err_flags, torch.int32)
+        if cache.err_flags.numel() < 1:
+            _bad(where, "err_flags is empty")
+
+
+def _ws_bytes(where: str, ws) -> int:
+    _tensor(where, "workspace", ws)
+    _on_gpu(where, workspace=ws)
+    return ws.numel() * ws.element_size()
+
+
+def _cache_on_gpu(where: str, cache: PagedCache) -> None:
+    _on_gpu(where, pool=cache.pool, block_table=cache.block_table, err_flags=cache.err_flags)
 
 
 def _ptr(t):
@@ -172,10 +230,34 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _weight_shapes(cfg: "Config") -> dict:
+    H = cfg.n_heads
+    return {"w_dq": (cfg.d_cq, cfg.d_model), "g_q": (cfg.d_cq,), "w_uq": (H * cfg.d_head, cfg.d_cq),
+            "w_qr": (H * cfg.d_rope, cfg.d_cq), "w_dkv": (cfg.d_c, cfg.d_model), "g_kv": (cfg.d_c,),
+            "w_kr": (cfg.d_rope, cfg.d_model), "w_uk": (H * cfg.d_head, cfg.d_c), "w_uv": (H * cfg.d_head, cfg.d_c)}
+
+
+def _weights_ok(where: str, cfg: "Config", w: dict, names) -> None:
+    shapes = _weight_shapes(cfg)
+    for n in names:
+        if w.get(n) is None:
+            _bad(where, f"weight {n} is missing")
+        _tensor(where, n, w[n], cfg.dtype, shapes[n])
+
+
 # ---------------------------------------------------------------------------
 def mla_cache_append(cfg: Config, cache: PagedCache, ckv_raw, kr_raw, g_kv, seq_idx, pos, stream=None) -> None:
     """Append rows [RMSNorm(ckv_raw[i]) ; RoPE(kr_raw[i], pos[i])] for sequences seq_idx."""
+    where = "mla_cache_append"
     n = ckv_raw.shape[0]
+    _cache_ok(where, cfg, cache, 0)
+    _tensor(where, "ckv_raw", ckv_raw, cfg.dtype, (n, cfg.d_c))
+    _tensor(where, "kr_raw", kr_raw, cfg.dtype, (n, cfg.d_rope))
+    _tensor(where, "g_kv", g_kv, cfg.dtype, (cfg.d_c,))
+    _tensor(where, "seq_idx", seq_idx, torch.int32, (n,))
+    _tensor(where, "pos", pos, torch.int32, (n,))
+    _on_gpu(where, ckv_raw=ckv_raw, kr_raw=kr_raw, g_kv=g_kv, seq_idx=seq_idx, pos=pos)
+    _cache_on_gpu(where, cache)
     _check(lib().mla_cache_append(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(ckv_raw), _ptr(kr_raw),
                                   _ptr(g_kv), _ptr(seq_idx), _ptr(pos), n, cache.block_table.shape[0],
                                   _stream(stream)), "mla_cache_append")
@@ -191,11 +273,17 @@ def mla_project_kv_workspace_size(cfg: Config, B: int, L: int) -> int:
 def mla_project_kv(cfg: Config, cache: PagedCache, weights: dict, h, start_pos: int = 0, ws=None,
                    stream=None) -> None:
     """[W^DKV ; W^KR] h for h [B, L, d_model], then append the rows at start_pos .. start_pos+L-1."""
+    where = "mla_project_kv"
+    _tensor(where, "h", h, cfg.dtype, (None, None, cfg.d_model))
     B, L = h.shape[0], h.shape[1]
+    _cache_ok(where, cfg, cache, B)
+    _weights_ok(where, cfg, weights, ("w_dkv", "w_kr", "g_kv"))
+    _on_gpu(where, h=h, **{k: weights[k] for k in ("w_dkv", "w_kr", "g_kv")})
+    _cache_on_gpu(where, cache)
     if ws is None:
         ws = _workspace(mla_project_kv_workspace_size(cfg, B, L), h.device)
     _check(lib().mla_project_kv(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), ctypes.byref(_weights(weights)),
-                                _ptr(h), B, L, start_pos, _ptr(ws), ws.numel(), _stream(stream)), "mla_project_kv")
+                                _ptr(h), B, L, start_pos, _ptr(ws), _ws_bytes(where, ws), _stream(stream)), where)
 
 
 def mla_prefill_workspace_size(cfg: Config, B: int, L: int, start_pos: int = 0) -> int:
@@ -211,13 +299,22 @@ def mla_prefill(cfg: Config, cache: PagedCache, weights: dict, h, out, start_pos
 
     attn_events: optional (start, stop) raw hipEvent_t handles recorded around
     the attention kernel (mla_prefill_profiled)."""
+    where = "mla_prefill"
+    _tensor(where, "h", h, cfg.dtype, (None, None, cfg.d_model))
     B, L = h.shape[0], h.shape[1]
+    _tensor(where, "out", out, cfg.dtype, (B, L, cfg.n_heads, cfg.d_head))
+    _cache_ok(where, cfg, cache, B)
+    _weights_ok(where, cfg, weights, tuple(_weight_shapes(cfg)))
+    _on_gpu(where, h=h, out=out, **{k: weights[k] for k in _weight_shapes(cfg)})
+    _cache_on_gpu(where, cache)
     if ws is None:
         ws = _workspace(mla_prefill_workspace_size(cfg, B, L, start_pos), h.device)
-    ev0, ev1 = attn_events if attn_events is not None else (None, None)
-    _check(lib().mla_prefill_profiled(ctypes.byref(cfg._c()), ctypes.byref(cache._c()),
-                                      ctypes.byref(_weights(weights)), _ptr(h), B, L, start_pos, _ptr(out), _ptr(ws),
-                                      ws.numel(), _stream(stream), ev0, ev1), "mla_prefill")
+    args = [ctypes.byref(cfg._c()), ctypes.byref(cache._c()), ctypes.byref(_weights(weights)), _ptr(h), B, L,
+            start_pos, _ptr(out), _ptr(ws), _ws_bytes(where, ws), _stream(stream)]
+    if attn_events is None:
+        _check(lib().mla_prefill(*args), where)
+    else:
+        _check(lib().mla_prefill_profiled(*args, *attn_events), where)
 
 
 def mla_output_projection_workspace_size(cfg: Config, T: int, width: int) -> int:
@@ -230,11 +327,18 @@ def mla_output_projection_workspace_size(cfg: Config, T: int, width: int) -> int
 def mla_output_projection(cfg: Config, x, w_o, u, ws=None, stream=None) -> None:
     """u [T, d_model] = x [T, width] W^O^T with W^O [d_model, width] (width = n_heads * d_head,
     or n_heads * d_c for the folded W^O')."""
+    where = "mla_output_projection"
+    _tensor(where, "x", x, cfg.dtype)
+    if x.dim() < 2:
+        _bad(where, "x must be [T, width] or [T, n_heads, d_head]")
     T, width = x.shape[0], x.numel() // max(x.shape[0], 1)
+    _tensor(where, "w_o", w_o, cfg.dtype, (cfg.d_model, width))
+    _tensor(where, "u", u, cfg.dtype, (T, cfg.d_model))
+    _on_gpu(where, x=x, w_o=w_o, u=u)
     if ws is None:
         ws = _workspace(max(mla_output_projection_workspace_size(cfg, T, width), 1), x.device)
     _check(lib().mla_output_projection(ctypes.byref(cfg._c()), _ptr(x), width, _ptr(w_o), _ptr(u), T, _ptr(ws),
-                                       ws.numel(), _stream(stream)), "mla_output_projection")
+                                       _ws_bytes(where, ws), _stream(stream)), where)
 
 
 def mla_decode_workspace_size(cfg: Config, B: int, s_q: int, max_kv_len: int) -> int:
@@ -254,10 +358,22 @@ def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope,
 
     attn_events: optional (start, stop) raw hipEvent_t handles recorded around
     the attention kernel (mla_decode_profiled)."""
+    where = "mla_decode"
+    _tensor(where, "q_nope", q_nope, cfg.dtype, (None, None, cfg.n_heads, cfg.d_head))
     B, s_q = q_nope.shape[0], q_nope.shape[1]
+    _tensor(where, "q_pe", q_pe, cfg.dtype, (B, s_q, cfg.n_heads, cfg.d_rope))
+    _tensor(where, "w_uk", w_uk, cfg.dtype, (cfg.n_heads * cfg.d_head, cfg.d_c))
+    _tensor(where, "w_uv", w_uv, cfg.dtype, (cfg.n_heads * cfg.d_head, cfg.d_c))
+    _tensor(where, "out", out, cfg.dtype, (B, s_q, cfg.n_heads, cfg.d_head))
+    _tensor(where, "kv_lens", kv_lens, torch.int32, (B,))
+    _cache_ok(where, cfg, cache, B)
+    _on_gpu(where, q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, out=out, kv_lens=kv_lens)
+    _cache_on_gpu(where, cache)
     if ws is None:
         ws = _workspace(mla_decode_workspace_size(cfg, B, s_q, max_kv_len), q_nope.device)
-    ev0, ev1 = attn_events if attn_events is not None else (None, None)
-    _check(lib().mla_decode_profiled(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens),
-                                     int(max_kv_len), B, s_q, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
-                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream), ev0, ev1), "mla_decode")
+    args = [ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens), int(max_kv_len), B, s_q, _ptr(q_nope),
+            _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(ws), _ws_bytes(where, ws), _stream(stream)]
+    if attn_events is None:
+        _check(lib().mla_decode(*args), where)
+    else:
+        _check(lib().mla_decode_profiled(*args, *attn_events), where)

@@ -53,11 +53,29 @@ def _bf_rms(x, g, eps):
     return [x[k] / math.sqrt(ms + eps) * g[k] for k in range(len(x))]
 
 
-def _bf_rope(x, pos, base):
+def _bf_theta(p, d, base, yarn=None):
+    """Frequency of pair p.  With ``yarn`` (s, alpha, beta, orig_ctx): count the
+    pair's turns over the original window, r = orig_ctx * theta / (2 pi); at
+    r <= alpha the frequency is divided by s, at r >= beta it is kept, and in
+    between the two are blended linearly in r."""
+    th = base ** (-2.0 * p / d)
+    if yarn is None:
+        return th
+    r = yarn["orig_ctx"] * th / (2.0 * math.pi)
+    if r <= yarn["alpha"]:
+        blend = 0.0
+    elif r >= yarn["beta"]:
+        blend = 1.0
+    else:
+        blend = (r - yarn["alpha"]) / (yarn["beta"] - yarn["alpha"])
+    return blend * th + (1.0 - blend) * (th / yarn["s"])
+
+
+def _bf_rope(x, pos, base, yarn=None):
     d = len(x)
     y = list(x)
     for p in range(d // 2):
-        th = pos * base ** (-2.0 * p / d)
+        th = pos * _bf_theta(p, d, base, yarn)
         c, s = math.cos(th), math.sin(th)
         # R = [[c, -s], [s, c]] applied to the column (x_2p, x_2p+1)
         y[2 * p] = c * x[2 * p] - s * x[2 * p + 1]
@@ -65,7 +83,30 @@ def _bf_rope(x, pos, base):
     return y
 
 
-def _bf_prefill(h, w, H, eps, base):
+def _bf_fp8_latent(x):
+    """c^KV as the FP8 cache holds it, one 128-value tile at a time: the
+    tile's power of two 2^e (smallest e with max|x| <= 448 * 2^e), each value
+    divided by it in float32, rounded by torch's float8_e4m3fn conversion and
+    multiplied back."""
+    out = []
+    for t0 in range(0, len(x), 128):
+        tile = [float(np.float32(v)) for v in x[t0:t0 + 128]]
+        amax = max(abs(v) for v in tile)
+        e = 0
+        if amax > 0:
+            while amax > 448.0 * 2.0 ** e:
+                e += 1
+            while amax <= 448.0 * 2.0 ** (e - 1):
+                e -= 1
+        q = torch.tensor([v / 2.0 ** e for v in tile], dtype=torch.float32).to(torch.float8_e4m3fn)
+        out += [float(v) * 2.0 ** e for v in q.to(torch.float64).tolist()]
+    return out
+
+
+def _bf_prefill(h, w, H, eps, base, yarn=None, kv_fp8=False):
+    """Steps (1)-(10) in scalar loops.  ``yarn``: YaRN frequencies on q^R and
+    k^R, every logit times (0.1 ln s + 1)^2.  ``kv_fp8``: c^KV read back
+    through the FP8 cache format (k^R untouched)."""
     W = {k: np.asarray(v).tolist() for k, v in w.items()}
     L = len(h)
     dh = len(W["w_uq"]) // H
@@ -77,14 +118,18 @@ def _bf_prefill(h, w, H, eps, base):
         qc = _bf_matvec(W["w_uq"], cq)                                       # (2)
         qr_all = _bf_matvec(W["w_qr"], cq)                                   # (3)
         ckv = _bf_rms(_bf_matvec(W["w_dkv"], hs[t]), W["g_kv"], eps)         # (5)
+        if kv_fp8:
+            ckv = _bf_fp8_latent(ckv)
         kc = _bf_matvec(W["w_uk"], ckv)                                      # (6)
-        kr = _bf_rope(_bf_matvec(W["w_kr"], hs[t]), t, base)                 # (7)
+        kr = _bf_rope(_bf_matvec(W["w_kr"], hs[t]), t, base, yarn)           # (7)
         vc = _bf_matvec(W["w_uv"], ckv)                                      # (9)
-        q.append([qc[i * dh:(i + 1) * dh] + _bf_rope(qr_all[i * dr:(i + 1) * dr], t, base)
+        q.append([qc[i * dh:(i + 1) * dh] + _bf_rope(qr_all[i * dr:(i + 1) * dr], t, base, yarn)
                   for i in range(H)])                                        # (4)
         k.append([kc[i * dh:(i + 1) * dh] + kr for i in range(H)])           # (8)
         v.append([vc[i * dh:(i + 1) * dh] for i in range(H)])
     scale = 1.0 / math.sqrt(dh + dr)
+    if yarn is not None:
+        scale *= (0.1 * math.log(yarn["s"]) + 1.0) ** 2
     out = np.zeros((L, H, dh))
     for t in range(L):                                                       # (10)
         for i in range(H):
@@ -471,6 +516,67 @@ def test_yarn_prefill_s1_equals_plain_prefill():
     b, rb = om.prefill(h, w, s.n_heads, s.rms_eps, s.rope_base, s.scale,
                        yarn=dict(s=1.0, alpha=1.0, beta=32.0, orig_ctx=4096))
     assert _rel(a, b) <= 1e-13 and _rel(ra, rb) <= 1e-13
+
+
+def test_yarn_prefill_matches_bruteforce():
+    """The whole prefill with YaRN at the page's s = 40, alpha = 1, beta = 32:
+    scalar loops with the ramp written out pair by pair, the same frequencies
+    on q^R and k^R and every logit times (0.1 ln s + 1)^2.  With d_h^R = 8,
+    base 10000 and a 4096-token original window the four pairs make
+    652, 65, 6.5 and 0.65 turns: two kept, one blended, one divided by s."""
+    y, _ = _yarn_page()
+    H, dr = 3, 8
+    w, h = _rand_setup(11, H=H, dr=dr, L=8)
+    turns = [y["orig_ctx"] * 10000.0 ** (-2.0 * p / dr) / (2 * math.pi) for p in range(dr // 2)]
+    assert turns[0] > y["beta"] and turns[1] > y["beta"] and y["alpha"] < turns[2] < y["beta"] and turns[3] < y["alpha"]
+    ref = _bf_prefill(h, w, H, 1e-6, 10000.0, yarn=y)
+    o, _ = om.prefill(h, w, H, 1e-6, 10000.0, scale=1.0 / math.sqrt(4 + dr), yarn=y)
+    assert _rel(o, ref) <= 1e-12
+    # the pin can tell YaRN from plain RoPE: each of its two parts moves the output
+    plain = _bf_prefill(h, w, H, 1e-6, 10000.0)
+    assert _rel(plain, ref) > 1e-3
+
+
+def test_yarn_prefill_parts_are_each_visible():
+    """Each half of YaRN alone (frequencies without the logit factor, the
+    factor without the frequencies) gives an output the brute force rejects,
+    so the pin above fails if either is dropped."""
+    y, _ = _yarn_page()
+    H, dr = 2, 8
+    w, h = _rand_setup(12, H=H, dr=dr, L=6)
+    ref = _bf_prefill(h, w, H, 1e-6, 10000.0, yarn=y)
+    sc = 1.0 / math.sqrt(4 + dr)
+    freq_only, _ = om.prefill(h, w, H, 1e-6, 10000.0, scale=sc / om.yarn_logit_factor(y["s"]), yarn=y)
+    factor_only, _ = om.prefill(h, w, H, 1e-6, 10000.0, scale=sc * om.yarn_logit_factor(y["s"]))
+    assert _rel(freq_only, ref) > 1e-3 and _rel(factor_only, ref) > 1e-4
+
+
+def test_fp8_prefill_matches_bruteforce():
+    """Prefill over an FP8 cache: scalar loops that quantise c^KV tile by tile
+    through torch's float8_e4m3fn with the power-of-two tile scale, leave k^R
+    in full precision, and attend over the dequantised rows (the notes page,
+    section 二(三): activations in FP8 with one scale per 1 x 128 tile)."""
+    H, dc = 2, 128
+    w, h = _rand_setup(13, H=H, dc=dc, L=5)
+    ref = _bf_prefill(h, w, H, 1e-6, 10000.0, kv_fp8=True)
+    o, rows = om.prefill(h, w, H, 1e-6, 10000.0, scale=1.0 / math.sqrt(4 + 2), kv_fp8=True)
+    assert _rel(o, ref) <= 1e-12
+    plain = _bf_prefill(h, w, H, 1e-6, 10000.0)
+    assert _rel(plain, ref) > 1e-4  # the quantisation is visible at this bar
+    # the cached k^R (last d_h^R values of each row) is not quantised
+    pos = np.arange(5)
+    kr = om.rope(np.asarray(h) @ np.asarray(w["w_kr"]).T, pos, 10000.0)
+    assert np.array_equal(rows[:, dc:], kr)
+
+
+def test_fp8_yarn_prefill_matches_bruteforce():
+    """Both options together, as the library allows them together."""
+    y, _ = _yarn_page()
+    H, dr, dc = 2, 8, 128
+    w, h = _rand_setup(14, H=H, dr=dr, dc=dc, L=5)
+    ref = _bf_prefill(h, w, H, 1e-6, 10000.0, yarn=y, kv_fp8=True)
+    o, _ = om.prefill(h, w, H, 1e-6, 10000.0, scale=1.0 / math.sqrt(4 + dr), yarn=y, kv_fp8=True)
+    assert _rel(o, ref) <= 1e-12
 
 
 # ---------------------------------------------------------------------------
