@@ -52,6 +52,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(2 * n):
             e = ctypes.c_void_p()
@@ -69,6 +70,22 @@ class HipEvents:
     def close(self):
         for e in self.ev:
             self.hip.hipEventDestroy(e)
+
+
+def settle(step, min_ms: float = 150.0) -> float:
+    """Run `step` untimed until at least min_ms of wall time has passed: from
+    idle the GPU needs some tens of milliseconds of sustained load before its
+    clock settles, whatever the caller's warm-up count.  Returns the time spent."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) * 1e3
+            if el >= min_ms:
+                return el
 
 
 def _up(a, dtype=torch.bfloat16):
@@ -115,6 +132,7 @@ def run_decode_bench(steps: int, warmup: int, fp8: bool = False):
         mla.mla_decode(cfg, caches[i % len(caches)], t["kv_lens"], max_kv, t["q_nope"], t["q_pe"], t["w_uk"],
                        t["w_uv"], out, ws=ws, attn_events=evs)
 
+    settle_ms = settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -133,7 +151,7 @@ def run_decode_bench(steps: int, warmup: int, fp8: bool = False):
     latent_bytes = int(inp.kv_lens.sum()) * cfg.row_bytes
     flops = int(inp.kv_lens.sum()) * cfg.n_heads * (cfg.row + cfg.d_c) * 2
     return dict(inp=inp, wall=wall, attn_ms=float(np.mean(attn_list)), attn_list=attn_list,
-                latent_bytes=latent_bytes, attn_flops=flops)
+                latent_bytes=latent_bytes, attn_flops=flops, settle_ms=settle_ms)
 
 
 def run_fp8_summary(steps: int, warmup: int, bf16_attn_ms: float) -> dict:
@@ -186,6 +204,7 @@ def run_prefill_bench(steps: int, warmup: int, form: int, L: int = 8192):
     out = torch.empty((1, L, s.n_heads, s.d_head), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mla.mla_prefill_workspace_size(cfg, 1, L), dtype=torch.uint8, device="cuda")
     ev = HipEvents(steps)
+    settle(lambda i: mla.mla_prefill(cfg, cache, w, h, out, ws=ws), 100.0)
     for _ in range(warmup):
         mla.mla_prefill(cfg, cache, w, h, out, ws=ws)
     torch.cuda.synchronize()
@@ -216,6 +235,7 @@ def run_output_projection_bench(steps: int, warmup: int) -> dict:
         u = torch.empty((T, s.d_model), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(max(mla.mla_output_projection_workspace_size(cfg, T, width), 256), dtype=torch.uint8,
                          device="cuda")
+        settle(lambda i: mla.mla_output_projection(cfg, x, w, u, ws=ws), 100.0)
         for _ in range(warmup):
             mla.mla_output_projection(cfg, x, w, u, ws=ws)
         torch.cuda.synchronize()
@@ -251,6 +271,7 @@ def run_down_projection_bench(steps: int, warmup: int) -> dict:
     cache = mla.PagedCache(torch.zeros((npages, s.page_size, cfg.row), dtype=torch.bfloat16, device="cuda"),
                            torch.from_numpy(bt).cuda())
     ws = torch.empty(max(mla.mla_project_kv_workspace_size(cfg, 1, L), 256), dtype=torch.uint8, device="cuda")
+    settle(lambda i: mla.mla_project_kv(cfg, cache, w, h, ws=ws), 100.0)
     for _ in range(warmup):
         mla.mla_project_kv(cfg, cache, w, h, ws=ws)
     torch.cuda.synchronize()
@@ -275,7 +296,11 @@ def run_other_decode(steps: int, warmup: int) -> dict:
     s = mi.V3
     cfg = mla.Config(**CFG_EXTRA)
     res = {}
-    for cid, name, s_q in ((4, "long_context_b4_131072", 1), (5, "ragged_b128_u1_32768_sq2", 2)):
+    for cid, name, s_q, desc in (
+            (4, "long_context_b4_131072", 1, "MLA decode step, B=4 sequences x (131072 cached + 1 new) tokens, "
+                                             "s_q=1, V3 heads, 64-token pages, shuffled block table"),
+            (5, "ragged_b128_u1_32768_sq2", 2, "MLA decode step, B=128 sequences, context ~ U{1..32768} + 2 new "
+                                               "tokens (causal pair), V3 heads, 64-token pages, shuffled block table")):
         ctx = mi.config_context_lens(cid)
         kv = (ctx + s_q).astype(np.int32)
         B, max_kv = len(kv), int(kv.max())
@@ -291,23 +316,43 @@ def run_other_decode(steps: int, warmup: int) -> dict:
         kvd = torch.from_numpy(kv).cuda()
         out = torch.empty((B, s_q, s.n_heads, s.d_head), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(mla.mla_decode_workspace_size(cfg, B, s_q, max_kv), dtype=torch.uint8, device="cuda")
-        for _ in range(warmup):
-            mla.mla_decode(cfg, cache, kvd, max_kv, q_nope, q_pe, w_uk, w_uv, out, ws=ws)
+        ev = HipEvents(steps)
+
+        def step(i, evs=None):
+            mla.mla_decode(cfg, cache, kvd, max_kv, q_nope, q_pe, w_uk, w_uv, out, ws=ws, attn_events=evs)
+
+        settle(step, 100.0)
+        for i in range(warmup):
+            step(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            mla.mla_decode(cfg, cache, kvd, max_kv, q_nope, q_pe, w_uk, w_uv, out, ws=ws)
+        for i in range(steps):
+            step(i)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
+        for i in range(steps):
+            step(i, ev.pair(i))
+        torch.cuda.synchronize()
+        kms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+        ev.close()
         nbytes = int(kv.sum()) * cfg.row * 2
         # keys each query sees (causal within the s_q new tokens)
         pairs = int(sum(int(k) - s_q + i + 1 for k in kv for i in range(s_q)))
         flops = pairs * s.n_heads * (cfg.row + cfg.d_c) * 2
-        res[name] = {"ms_per_step": round(ms, 4), "latent_bytes": nbytes,
-                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        # the binding roof: bytes at the HBM peak or FLOPs at the MFMA peak, whichever takes longer
+        t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        if t_hbm >= t_mfma:
+            roof = {"bound": "hbm", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": round(flops / (kms * 1e-3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+        roof.update(frac=round(roof["achieved"] / roof["peak"], 4), kernel="attn_bf16_kernel",
+                    kernel_ms=round(kms, 5), t_roof_ms=round(max(t_hbm, t_mfma) * 1e3, 5))
+        res[name] = {"workload": desc, "ms_per_step": round(ms, 4), "latent_bytes": nbytes, "attn_flops": flops,
+                     "gbs_step": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "tflops_step": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_roof_step": round(max(t_hbm, t_mfma) * 1e3 / ms, 4), "roofline": roof}
         del pool, cache, out, ws
         torch.cuda.empty_cache()
     return res
@@ -372,32 +417,97 @@ def run_prefill_summary(args) -> dict:
 
 def measured_traffic(path: str = os.path.join(ROOT, "profiles", "attn_bf16_decode_b64_ctx4096_traffic.md")):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing or the kernel source changed after it was taken."""
-    import hashlib
+    None when it is missing or the kernel's sources changed after it was taken."""
     try:
         kv = dict(l.split(":", 1) for l in open(path).read().splitlines() if l.startswith(("traffic_", "source_")))
     except OSError:
         return None
-    src = os.path.join(ROOT, "head_latent_attention_06_amd", "csrc", "mla_attn.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256", "").strip():
+    if attention_sources_sha256() != kv.get("source_sha256", "").strip():
         return None
     return int(kv["traffic_bytes_per_launch"].strip())
+
+
+def attention_sources_sha256() -> str:
+    """One hash over the sources the decode attention kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("mla_attn.hip", "mla_plan.h", "mla_device.h", "mla_kernels.h"):
+        h.update(open(os.path.join(ROOT, "head_latent_attention_06_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def run_ceilings(steps: int = 20) -> dict:
+    """Measured ceilings on this GPU: a plain streaming read of 4 GiB (the
+    library's own read kernel) and the library's large-tile bf16 GEMM at
+    8192 x 8192 x 8192 (through the output-projection entry point)."""
+    res = {}
+    src = torch.ones(1 << 31, dtype=torch.int16, device="cuda")  # 4 GiB
+    nbytes = src.numel() * 2
+    settle(lambda i: mla.mla_stream_read(src), 100.0)
+    ev = HipEvents(steps)
+    hip_stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(steps):
+        ev.hip.hipEventRecord(ev.ev[2 * i], hip_stream)
+        mla.mla_stream_read(src)
+        ev.hip.hipEventRecord(ev.ev[2 * i + 1], hip_stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    res["hbm_read"] = {"kernel": "stream_read_kernel", "bytes": nbytes, "ms": round(ms, 4),
+                       "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "frac_of_spec": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del src
+    n = 8192
+    cfg = mla.Config(d_model=n, **CFG_EXTRA)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn((n, n), device="cuda", generator=g).bfloat16()
+    w = (torch.randn((n, n), device="cuda", generator=g) * n ** -0.5).bfloat16()
+    u = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(mla.mla_output_projection_workspace_size(cfg, n, n), 256), dtype=torch.uint8, device="cuda")
+    settle(lambda i: mla.mla_output_projection(cfg, x, w, u, ws=ws), 100.0)
+    ev = HipEvents(steps)
+    for i in range(steps):
+        ev.hip.hipEventRecord(ev.ev[2 * i], hip_stream)
+        mla.mla_output_projection(cfg, x, w, u, ws=ws)
+        ev.hip.hipEventRecord(ev.ev[2 * i + 1], hip_stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    flops = 2 * n ** 3
+    res["gemm_bf16"] = {"kernel": "gemm_big_kernel", "shape": [n, n, n], "operands": "N(0,1) x N(0,1/n), bf16",
+                        "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                        "frac_of_spec": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del x, w, u, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def _vs_measured(roof: dict, ceil: dict) -> None:
+    """Add the fraction of the measured ceiling of the same unit to a roofline."""
+    if roof.get("unit") == "GB/s" and "hbm_read" in ceil:
+        roof["frac_of_measured"] = round(roof["achieved"] / ceil["hbm_read"]["gbs"], 4)
+    elif roof.get("unit") == "TFLOP/s" and "gemm_bf16" in ceil:
+        roof["frac_of_measured"] = round(roof["achieved"] / ceil["gemm_bf16"]["tflops"], 4)
+
+
+LEGS = ("decode", "output_projection", "fp8", "other_decode", "prefill", "down_projection", "ceilings", "cpu")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # From idle the GPU needs ~50 ms of sustained load to reach its steady
-    # clock: decode steps after 20 warm-up steps take ~130 us, after 500 (or
-    # 2000) ~110 us.  500 decode steps are ~60 ms.
-    ap.add_argument("--warmup", type=int, default=500)
+    # Every leg first runs its step untimed for at least 100-150 ms (settle()),
+    # so the GPU clock has settled whatever the warm-up count.
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS) + " (the headline decode always runs "
+                         "unless --prefill-only)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill workload (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--other-decode", action="store_true",
-                    help="also time the long-context and ragged decode workloads (not in the default run)")
     ap.add_argument("--yarn", action="store_true",
                     help="run both workloads with the YaRN long-context settings (s=40, alpha=1, beta=32, 4K window)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -414,6 +524,14 @@ def main():
         return
     if args.yarn:
         CFG_EXTRA.update(YARN)
+    legs = set(args.legs.split(","))
+    unknown = legs - set(LEGS)
+    if unknown:
+        ap.error(f"unknown legs {sorted(unknown)}")
+    if args.no_prefill:
+        legs -= {"prefill", "down_projection"}
+    if args.no_cpu_baseline:
+        legs -= {"cpu"}
 
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill_summary(args)}), flush=True)
@@ -430,20 +548,35 @@ def main():
                                "n_h=128, d_h=128, d_c=512, d_h^R=64, 64-token pages, shuffled block table",
                    "global_batch": 64, "seq_len": 4097, "parallelism": "none (1 GPU)",
                    "yarn": bool(CFG_EXTRA)},
+        "settle_ms": round(d["settle_ms"], 1),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(d["attn_ms"], 5),
                      "algorithmic_bytes": d["latent_bytes"],
                      "mfma_tflops": round(d["attn_flops"] / (d["attn_ms"] * 1e-3) / 1e12, 1)},
     }
-    res["output_projection"] = run_output_projection_bench(args.steps, args.warmup)
-    res["fp8_cache"] = run_fp8_summary(max(20, args.steps // 2), max(20, args.warmup // 4), d["attn_ms"])
-    if args.other_decode:
-        res["other_decode"] = run_other_decode(max(10, args.steps // 4), max(20, args.warmup // 4))
-    if not args.no_prefill:
+    if "output_projection" in legs:
+        res["output_projection"] = run_output_projection_bench(args.steps, args.warmup)
+    if "fp8" in legs:
+        res["fp8_cache"] = run_fp8_summary(max(20, args.steps // 2), max(20, args.warmup // 2), d["attn_ms"])
+    if "other_decode" in legs:
+        res["other_decode"] = run_other_decode(max(10, args.steps // 4), max(10, args.warmup // 2))
+    if "prefill" in legs:
         res["prefill"] = run_prefill_summary(args)
+    if "down_projection" in legs:
         res["down_projection"] = run_down_projection_bench(20, 10)
-    if not args.no_cpu_baseline:
+    if "ceilings" in legs:
+        ceil = run_ceilings()
+        res["measured_ceilings"] = ceil
+        _vs_measured(res["roofline"], ceil)
+        for sub in ("fp8_cache", "prefill"):
+            if sub in res:
+                _vs_measured(res[sub]["roofline"], ceil)
+        if "prefill" in res:
+            _vs_measured(res["prefill"]["absorbed_form"]["roofline"], ceil)
+        for r in res.get("other_decode", {}).values():
+            _vs_measured(r["roofline"], ceil)
+    if "cpu" in legs:
         res["cpu_baseline"] = cpu_baseline(d["inp"], args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

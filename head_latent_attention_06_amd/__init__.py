@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_RANGE, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
 MLA_F32, MLA_BF16 = 0, 1
 PREFILL_AUTO, PREFILL_ABSORBED, PREFILL_EXPLICIT = 0, 1, 2
-ABI_VERSION = 4  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
+ABI_VERSION = 5  # MLA_ABI_VERSION of the include/mla.h this binding mirrors
 MLA_FLAG_BAD_PAGE, MLA_FLAG_BAD_POS, MLA_FLAG_BAD_LEN, MLA_FLAG_BAD_SEQ = 1, 2, 4, 8
 
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "mla_decode_workspace_size": (I32, [CP, I32, I32, I32, ctypes.POINTER(SZ)]),
             "mla_decode": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
             "mla_decode_num_splits": (I32, [CP, I32, I32, I32]),
+            "mla_stream_read": (I32, [P, ctypes.c_int64, P, P]),
             "mla_decode_profiled": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P, P, P]),
             "mla_prefill_profiled": (I32, [CP, KP, WP, P, I32, I32, I32, P, P, SZ, P, P, P]),
             "mla_output_projection_workspace_size": (I32, [CP, I32, I32, ctypes.POINTER(SZ)]),
@@ -352,13 +353,7 @@ def mla_decode_num_splits(cfg: Config, B: int, s_q: int, max_kv_len: int) -> int
     return int(lib().mla_decode_num_splits(ctypes.byref(cfg._c()), B, s_q, max_kv_len))
 
 
-def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope, q_pe, w_uk, w_uv, out, ws=None,
-               stream=None, attn_events=None) -> None:
-    """One decode step: q_nope [B, s_q, H, d_head], q_pe [B, s_q, H, d_rope] -> out [B, s_q, H, d_head].
-
-    attn_events: optional (start, stop) raw hipEvent_t handles recorded around
-    the attention kernel (mla_decode_profiled)."""
-    where = "mla_decode"
+def _decode_inputs_ok(where, cfg, cache, kv_lens, q_nope, q_pe, w_uk, w_uv, out):
     _tensor(where, "q_nope", q_nope, cfg.dtype, (None, None, cfg.n_heads, cfg.d_head))
     B, s_q = q_nope.shape[0], q_nope.shape[1]
     _tensor(where, "q_pe", q_pe, cfg.dtype, (B, s_q, cfg.n_heads, cfg.d_rope))
@@ -369,6 +364,17 @@ def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope,
     _cache_ok(where, cfg, cache, B)
     _on_gpu(where, q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, out=out, kv_lens=kv_lens)
     _cache_on_gpu(where, cache)
+    return B, s_q
+
+
+def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope, q_pe, w_uk, w_uv, out, ws=None,
+               stream=None, attn_events=None) -> None:
+    """One decode step: q_nope [B, s_q, H, d_head], q_pe [B, s_q, H, d_rope] -> out [B, s_q, H, d_head].
+
+    attn_events: optional (start, stop) raw hipEvent_t handles recorded around
+    the attention kernel (mla_decode_profiled)."""
+    where = "mla_decode"
+    B, s_q = _decode_inputs_ok(where, cfg, cache, kv_lens, q_nope, q_pe, w_uk, w_uv, out)
     if ws is None:
         ws = _workspace(mla_decode_workspace_size(cfg, B, s_q, max_kv_len), q_nope.device)
     args = [ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens), int(max_kv_len), B, s_q, _ptr(q_nope),
@@ -377,3 +383,11 @@ def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope,
         _check(lib().mla_decode(*args), where)
     else:
         _check(lib().mla_decode_profiled(*args, *attn_events), where)
+
+
+def mla_stream_read(src, stream=None) -> None:
+    """Read all of src (a contiguous GPU tensor) once: the HBM read ceiling."""
+    where = "mla_stream_read"
+    _tensor(where, "src", src)
+    _on_gpu(where, src=src)
+    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(), None, _stream(stream)), where)

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "mla.h"
 #include "mla_kernels.h"
 
@@ -92,9 +93,15 @@ int32_t max_chunk_keys(const mla_config* c) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Upper bound on plan items for n_rows rows of at most max_kv visible keys.
+// Chunks capped at max_chunk_keys: at most n_rows * ceil(max_kv / cap).  Else
+// chunks of at least max(MIN_CHUNK, T / tgt) keys for T visible keys in all
+// and tgt <= target * RAGGED_FACTOR: a row of v keys takes at most
+// v / chunk + 1 of them, so n_rows + min(tgt, T / MIN_CHUNK) in all.
 int64_t max_plan_items(const mla_config* c, int64_t n_rows, int32_t max_kv, int32_t target) {
   const int64_t by_cap = n_rows * ceil_div(max_kv, max_chunk_keys(c));
-  const int64_t by_target = target > 0 ? n_rows + (int64_t)target * RAGGED_FACTOR : 0;
+  int64_t spread = (int64_t)target * RAGGED_FACTOR;
+  if (ceil_div(n_rows * (int64_t)max_kv, MIN_CHUNK) < spread) spread = ceil_div(n_rows * (int64_t)max_kv, MIN_CHUNK);
+  const int64_t by_target = target > 0 ? n_rows + spread : 0;
   const int64_t m = by_target > by_cap ? by_target : by_cap;
   // the attention grid spreads the items over the 8 XCDs in equal runs, which
   // can leave up to 7 empty slots: round up to whole rounds of 8
@@ -109,8 +116,9 @@ struct DecodeWs {
   int64_t max_items;
 };
 
+// items > 0: that many split slots instead of the bound for these sizes
 DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, int32_t max_kv, void* ws,
-                       size_t* total) {
+                       size_t* total, int64_t items = 0) {
   Carve cv(ws);
   DecodeWs d{};
   const int64_t rows = (int64_t)B * s_q, H = c->n_heads, row = c->d_c + c->d_rope;
@@ -118,7 +126,7 @@ DecodeWs decode_layout(const mla_config* c, bool bf16, int32_t B, int32_t s_q, i
   d.q_lat = cv.take(rows * H * c->d_c * e);
   d.o_lat = cv.take(rows * H * c->d_c * e);
   if (bf16) {
-    d.max_items = max_plan_items(c, rows, max_kv, DECODE_TARGET_ITEMS);
+    d.max_items = items > 0 ? items : max_plan_items(c, rows, max_kv, DECODE_TARGET_ITEMS);
     d.plan = (int32_t*)cv.take(plan_ints(rows, d.max_items) * 4);
     d.part_o = cv.take(d.max_items * H * c->d_c * 2);
     d.part_ml = (float*)cv.take(d.max_items * H * 2 * 4);
@@ -568,28 +576,38 @@ mla_status mla_decode(const mla_config* cfg, const mla_kv_cache* cache, const in
                              stream, nullptr, nullptr);
 }
 
-mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
-                               int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
-                               const void* w_uk, const void* w_uv, void* out, void* ws, size_t ws_bytes,
-                               void* stream, void* attn_start, void* attn_stop) {
-  bool bf16;
-  mla_status s = check_cfg(cfg, &bf16);
+}  // extern "C"
+
+namespace {
+
+// Checks of mla_decode's arguments other than the workspace; *empty when
+// there is nothing to do (B == 0 or s_q == 0).
+mla_status decode_check(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens, int32_t max_kv_len,
+                        int32_t B, int32_t s_q, const void* q_nope, const void* q_pe, const void* w_uk,
+                        const void* w_uv, void* out, bool* bf16, bool* empty) {
+  mla_status s = check_cfg(cfg, bf16);
   if (s != MLA_OK) return s;
   if ((s = check_cache(cfg, cache)) != MLA_OK) return s;
   if (B < 0 || s_q < 0) return MLA_ERR_INVALID_ARG;
-  if (B == 0 || s_q == 0) return MLA_OK;
-  if (!kv_lens || !q_nope || !q_pe || !w_uk || !w_uv || !out || !ws) return MLA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, out, ws};
+  *empty = B == 0 || s_q == 0;
+  if (*empty) return MLA_OK;
+  if (!kv_lens || !q_nope || !q_pe || !w_uk || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
   if (max_kv_len < s_q) return MLA_ERR_INVALID_ARG;
   if ((int64_t)max_kv_len > (int64_t)cache->max_pages_per_seq * cfg->page_size || max_kv_len > (1 << 30))
     return MLA_ERR_OUT_OF_RANGE;
   if ((int64_t)B * s_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
-  size_t need;
-  DecodeWs d = decode_layout(cfg, bf16, B, s_q, max_kv_len, ws, &need);
-  if (need > ws_bytes) return MLA_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  return MLA_OK;
+}
+
+// The decode launches over a carved workspace.
+mla_status decode_run(const mla_config* cfg, bool bf16, const mla_kv_cache* cache, const int32_t* kv_lens,
+                      int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                      const void* w_uk, const void* w_uv, void* out, const DecodeWs& d, hipStream_t st,
+                      void* attn_start, void* attn_stop) {
+  mla_status s;
   const int rows = B * s_q, H = cfg->n_heads;
   AttnArgs a = attn_args(cfg, cache, d.q_lat, cfg->d_c, q_pe, cfg->d_rope, kv_lens, 0, max_kv_len, B, s_q);
   a.longest_first = 0;
@@ -606,6 +624,25 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
     return s;
   }
   return attend(cfg, bf16, a, DECODE_TARGET_ITEMS, true, true, w_uv, out, st, attn_start, attn_stop);
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                               int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, void* out, void* ws, size_t ws_bytes,
+                               void* stream, void* attn_start, void* attn_stop) {
+  bool bf16, empty;
+  mla_status s = decode_check(cfg, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, &bf16, &empty);
+  if (s != MLA_OK || empty) return s;
+  if (!ws || !aligned16(ws)) return MLA_ERR_INVALID_ARG;
+  size_t need;
+  DecodeWs d = decode_layout(cfg, bf16, B, s_q, max_kv_len, ws, &need);
+  if (need > ws_bytes) return MLA_ERR_WORKSPACE;
+  return decode_run(cfg, bf16, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, d,
+                    (hipStream_t)stream, attn_start, attn_stop);
 }
 
 // Split of the output projection's reduction: enough workgroups to stream W^O

@@ -58,8 +58,13 @@ __device__ inline void plan_body(const AttnArgs& a, int32_t* plan, int32_t targe
     const int M = max(max(red_max[0], red_max[1]), max(red_max[2], red_max[3]));
     int chunk = max_chunk;
     if (target_items > 0 && T > 0) {
-      // ragged batches get four times as many, smaller, chunks to even out
-      const long long tgt = (T * 4 >= 3LL * n_rows * M) ? target_items : 4LL * target_items;
+      // ragged batches get four times as many, smaller, chunks to even out;
+      // never more than the item slots the caller provided (max_items, of
+      // which 7 stay free for the XCD runs below) can hold: with chunks of at
+      // least T / tgt keys a row of v keys takes at most v / chunk + 1 items
+      long long tgt = (T * 4 >= 3LL * n_rows * M) ? target_items : 4LL * target_items;
+      const long long room = (long long)a.max_items - 7 - n_rows;
+      tgt = max(1LL, min(tgt, room));
       const long long c = (T + tgt - 1) / tgt;
       chunk = (int)min<long long>(max_chunk, max<long long>(min_chunk, (c + 31) / 32 * 32));
     }

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum {
   MLA_OK = 0,
@@ -247,6 +247,14 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
 mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
                                 const void* h, int32_t B, int32_t L, int32_t start_pos, void* out, void* ws,
                                 size_t ws_bytes, void* stream, void* attn_start, void* attn_stop);
+
+/* Measurement helper (not part of the attention arithmetic): read `bytes`
+ * bytes of device memory at src once, as a plain streaming kernel, so a
+ * caller can time the HBM read ceiling the decode kernel is compared with.
+ * bytes > 0 and src 16-byte aligned, else MLA_ERR_INVALID_ARG.  `sink` (may
+ * be NULL, else one writable uint32) is written only in the practically
+ * impossible case that the XOR of all words read equals 0x9E3779B9. */
+mla_status mla_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 
 /* Upper bound on the attention work items (split partial slots) mla_decode
  * plans for these sizes; the device plan cuts each query row's visible keys

@@ -209,20 +209,23 @@ def absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, scale: float, heads=
     """
     q_c, q_r, c, k_r = _f64(q_c), _f64(q_r), _f64(c), _f64(k_r)
     T, H, dh = q_c.shape
-    N = c.shape[0]
+    N, dc = c.shape
     heads = list(range(H)) if heads is None else list(heads)
-    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
-    visible = np.arange(N)[None, :] <= np.asarray(q_pos, np.int64)[:, None]
-    out = np.zeros((T, len(heads), dh), F64)
-    for n, i in enumerate(heads):
-        q_lat = q_c[:, i] @ w_uk[i * dh:(i + 1) * dh]          # [T, d_c]
-        s = (q_lat @ c.T + q_r[:, i] @ k_r.T) * scale
-        s = np.where(visible, s, -np.inf)
-        s = s - s.max(axis=1, keepdims=True)
-        e = np.exp(s)
-        a = e / e.sum(axis=1, keepdims=True)
-        out[:, n] = (a @ c) @ w_uv[i * dh:(i + 1) * dh].T
-    return out
+    nh = len(heads)
+    sel = slice(None) if heads == list(range(H)) else heads
+    w_uk = _f64(w_uk).reshape(H, dh, dc)[sel]                # W_i^UK, [n, d_h, d_c]
+    w_uv = _f64(w_uv).reshape(H, dh, dc)[sel]                # W_i^UV
+    visible = np.arange(N)[None, None, :] <= np.asarray(q_pos, np.int64)[:, None, None]
+    # q_lat_{t,i} = W_i^UK^T q^C_{t,i}, all selected heads at once ([n, T, d_c])
+    q_lat = np.matmul(q_c[:, sel].transpose(1, 0, 2), w_uk)
+    s = (q_lat.transpose(1, 0, 2).reshape(T * nh, dc) @ c.T + q_r[:, sel].reshape(T * nh, -1) @ k_r.T) * scale
+    s = np.where(visible, s.reshape(T, nh, N), -np.inf)
+    s = s - s.max(axis=2, keepdims=True)
+    e = np.exp(s)
+    a = e / e.sum(axis=2, keepdims=True)
+    o_lat = (a.reshape(T * nh, N) @ c).reshape(T, nh, dc)     # sum_j a_j c_j
+    # o_{t,i} = W_i^UV o_lat_{t,i}
+    return np.matmul(o_lat.transpose(1, 0, 2), w_uv.transpose(0, 2, 1)).transpose(1, 0, 2)
 
 
 # ---------------------------------------------------------------------------

@@ -177,6 +177,9 @@ def test_p1_absorbed_equals_explicit(seed):
     a = om.explicit_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.3)
     b = om.absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.3)
     assert _rel(b, a) <= 1e-12
+    # a subset of heads, in another order, is those heads of the whole
+    sub = om.absorbed_attention(q_c, q_r, c, k_r, w_uk, w_uv, q_pos, 0.3, heads=[3, 1])
+    assert _rel(sub, a[:, [3, 1]]) <= 1e-12
 
 
 # ---------------------------------------------------------------------------
