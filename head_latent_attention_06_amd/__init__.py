@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "mla_decode_workspace_size": (I32, [CP, I32, I32, I32, ctypes.POINTER(SZ)]),
             "mla_decode": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
             "mla_decode_num_splits": (I32, [CP, I32, I32, I32]),
+            "mla_decode_noalloc": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P]),
             "mla_stream_read": (I32, [P, ctypes.c_int64, P, P]),
             "mla_decode_profiled": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P, P, P]),
             "mla_prefill_profiled": (I32, [CP, KP, WP, P, I32, I32, I32, P, P, SZ, P, P, P]),
@@ -365,6 +366,17 @@ def _decode_inputs_ok(where, cfg, cache, kv_lens, q_nope, q_pe, w_uk, w_uv, out)
     _on_gpu(where, q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, out=out, kv_lens=kv_lens)
     _cache_on_gpu(where, cache)
     return B, s_q
+
+
+def mla_decode_noalloc(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope, q_pe, w_uk, w_uv, out,
+                       stream=None) -> None:
+    """mla_decode with the library's per-GPU scratch array as its workspace
+    (allocates nothing; calls on one GPU must not overlap)."""
+    where = "mla_decode_noalloc"
+    B, s_q = _decode_inputs_ok(where, cfg, cache, kv_lens, q_nope, q_pe, w_uk, w_uv, out)
+    _check(lib().mla_decode_noalloc(ctypes.byref(cfg._c()), ctypes.byref(cache._c()), _ptr(kv_lens),
+                                    int(max_kv_len), B, s_q, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                                    _ptr(out), _stream(stream)), where)
 
 
 def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope, q_pe, w_uk, w_uv, out, ws=None,

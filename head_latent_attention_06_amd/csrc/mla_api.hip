@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_kernels.h"
@@ -626,6 +628,63 @@ mla_status decode_run(const mla_config* cfg, bool bf16, const mla_kv_cache* cach
   return attend(cfg, bf16, a, DECODE_TARGET_ITEMS, true, true, w_uv, out, st, attn_start, attn_stop);
 }
 
+// ---- decode without allocation: the workspace is a scratch array in each
+// GPU's memory, found once per device with hipGetSymbolAddress (in host code
+// the array's name is not a device address).
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[MLA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+mla_status scratch_of_device(hipStream_t st, void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (st) {  // the stream must belong to the current device
+    hipDevice_t sd;
+    if (hipStreamGetDevice(st, &sd) != hipSuccess) return MLA_ERR_HIP;
+    if ((int)sd != dev) return MLA_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MLA_ERR_HIP;
+    g_scratch[dev] = q;
+  }
+  *p = g_scratch[dev];
+  return MLA_OK;
+}
+
+// The scratch layout for these sizes: the usual decode workspace, with fewer
+// split slots when the usual bound does not fit (the plan then makes fewer,
+// longer chunks of ragged batches).  MLA_ERR_WORKSPACE when even the fewest
+// slots the plan can work with do not fit.
+mla_status noalloc_layout(const mla_config* cfg, bool bf16, int32_t B, int32_t s_q, int32_t max_kv, void* base,
+                          DecodeWs* d) {
+  const size_t cap = MLA_DECODE_NOALLOC_SCRATCH_BYTES;
+  size_t need;
+  *d = decode_layout(cfg, bf16, B, s_q, max_kv, base, &need);
+  if (need <= cap) return MLA_OK;
+  if (!bf16) return MLA_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * s_q;
+  // slots the plan needs at least: every row one item (and 7 for the XCD
+  // runs), and every row cut at the chunk cap
+  const int64_t least = std::max(rows + 8, rows * ceil_div(max_kv, max_chunk_keys(cfg)) + 7);
+  const size_t per_item = (size_t)cfg->n_heads * cfg->d_c * 2 + (size_t)cfg->n_heads * 2 * 4 + 16;
+  int64_t items = d->max_items - (int64_t)((need - cap + per_item - 1) / per_item);
+  items = items / 8 * 8;
+  for (; items >= least; items -= 8) {
+    *d = decode_layout(cfg, bf16, B, s_q, max_kv, base, &need, items);
+    if (need <= cap) return MLA_OK;
+  }
+  return MLA_ERR_WORKSPACE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -643,6 +702,21 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
   if (need > ws_bytes) return MLA_ERR_WORKSPACE;
   return decode_run(cfg, bf16, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, d,
                     (hipStream_t)stream, attn_start, attn_stop);
+}
+
+mla_status mla_decode_noalloc(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                              int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                              const void* w_uk, const void* w_uv, void* out, void* stream) {
+  bool bf16, empty;
+  mla_status s = decode_check(cfg, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, &bf16, &empty);
+  if (s != MLA_OK || empty) return s;
+  DecodeWs d;
+  if ((s = noalloc_layout(cfg, bf16, B, s_q, max_kv_len, nullptr, &d)) != MLA_OK) return s;  // sizes first
+  void* base;
+  if ((s = scratch_of_device((hipStream_t)stream, &base)) != MLA_OK) return s;
+  if ((s = noalloc_layout(cfg, bf16, B, s_q, max_kv_len, base, &d)) != MLA_OK) return s;
+  return decode_run(cfg, bf16, cache, kv_lens, max_kv_len, B, s_q, q_nope, q_pe, w_uk, w_uv, out, d,
+                    (hipStream_t)stream, nullptr, nullptr);
 }
 
 // Split of the output projection's reduction: enough workgroups to stream W^O

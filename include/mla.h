@@ -21,7 +21,8 @@
  *    owns and allocates every buffer (cache pool, workspace, outputs); the
  *    library never allocates, frees or synchronises, and keeps no mutable
  *    global state, so calls on different streams may run concurrently as long
- *    as they touch disjoint buffers.
+ *    as they touch disjoint buffers.  The one exception is
+ *    mla_decode_noalloc, whose workspace is a per-GPU array of the library.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the default stream).  MLA_OK means "enqueued".
  *  - Argument, shape and dtype errors are detected on the host BEFORE any
@@ -247,6 +248,31 @@ mla_status mla_decode_profiled(const mla_config* cfg, const mla_kv_cache* cache,
 mla_status mla_prefill_profiled(const mla_config* cfg, const mla_kv_cache* cache, const mla_weights* w,
                                 const void* h, int32_t B, int32_t L, int32_t start_pos, void* out, void* ws,
                                 size_t ws_bytes, void* stream, void* attn_start, void* attn_stop);
+
+/* Decode without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks and result as mla_decode, without the
+ * workspace: the library keeps one scratch array of
+ * MLA_DECODE_NOALLOC_SCRATCH_BYTES in the memory of each GPU it is loaded on
+ * (held until the process ends) and carves the decode workspace out of it.
+ * When the usual workspace for these sizes does not fit, fewer split slots
+ * are used (the plan then cuts ragged batches into fewer, longer chunks; the
+ * result is the same up to rounding); when even that does not fit (with
+ * the V3 shapes and 64-token pages: more than 336 query rows B * s_q, fewer
+ * for contexts past 98,240 tokens, e.g. 252 at 131,073) the call returns
+ * MLA_ERR_WORKSPACE before any launch.  Nothing in the array needs to start at zero: every call
+ * writes its plan, queries and partials before reading them.
+ *  - The array is shared by every call on a GPU and keeps the last call's
+ *    contents: calls that overlap on one GPU (different streams without
+ *    ordering, or threads) race and corrupt each other's results.  Serialise
+ *    them (one stream, or events).
+ *  - `stream` must belong to the current device (MLA_ERR_INVALID_ARG if not).
+ *  - No hipMalloc, hipFree or other allocating call is made; the first call on
+ *    a device looks up the array's device address (hipGetSymbolAddress). */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+mla_status mla_decode_noalloc(const mla_config* cfg, const mla_kv_cache* cache, const int32_t* kv_lens,
+                              int32_t max_kv_len, int32_t B, int32_t s_q, const void* q_nope, const void* q_pe,
+                              const void* w_uk, const void* w_uv, void* out, void* stream);
 
 /* Measurement helper (not part of the attention arithmetic): read `bytes`
  * bytes of device memory at src once, as a plain streaming kernel, so a

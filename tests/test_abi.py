@@ -162,3 +162,19 @@ def test_fp8_cache_config(lib):
     bad = _cfg()
     bad.kv_fp8 = 2
     assert lib.mla_decode_workspace_size(ctypes.byref(bad), 1, 1, 10, ctypes.byref(n)) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_before_launch(lib):
+    """mla_decode_noalloc checks its sizes against the scratch array before it
+    touches the device: too many query rows, or a context that needs more
+    split slots than the array holds, return MLA_ERR_WORKSPACE."""
+    c = ctypes.byref(_cfg())
+    for B, max_kv in ((1024, 10), (1, 1 << 30)):
+        k = ctypes.byref(_cache(pages=1 << 24, maxp=(max_kv + 63) // 64))
+        st = lib.mla_decode_noalloc(c, k, FAKE, max_kv, B, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+        assert st == mla.MLA_ERR_WORKSPACE, (B, max_kv, st)
+    # the argument checks of mla_decode come first
+    k = ctypes.byref(_cache())
+    assert lib.mla_decode_noalloc(c, k, None, 100, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_noalloc(c, k, FAKE, 100, 2, 1, FAKE + 2, FAKE, FAKE, FAKE, FAKE, None) == \
+        mla.MLA_ERR_INVALID_ARG
