@@ -162,12 +162,28 @@ mla_status prefill_form(const mla_config* c, bool bf16, int32_t L, int32_t start
   return MLA_OK;
 }
 
-// [W^DKV ; W^KR] h has few output columns (d_c + d_rope): with too few
-// 256 x 192 tiles to fill the chip, the reduction over d_model runs as two
-// halves in one launch of twice the tiles and the append adds them.
-int kv_ksplit(const mla_config* c, bool bf16, int64_t T) {
-  const int64_t row = c->d_c + c->d_rope;
-  return bf16 && c->d_model % 128 == 0 && 2 * ((T + 255) / 256) * ((row + 191) / 192) <= 256 ? 2 : 1;
+// [W^DKV ; W^KR] h has few output columns (d_c + d_rope): with fewer
+// 256 x 192 tiles than CUs it runs in the stream-K form: kv_sk_groups()
+// groups of one workgroup per column tile (at most SK_MAX_WGS workgroups in
+// all, a multiple of 8 groups so each XCD holds whole groups, each group
+// with at least SK_MIN_SLICES k slices) share its (row tile, k slice) units
+// equally and write partial sums that the append adds.  kv_parts() is the
+// number of partial buffers (1: one plain product).
+constexpr int SK_MAX_WGS = 256, SK_MIN_SLICES = 48;
+int kv_sk_groups(const mla_config* c, bool bf16, int64_t T) {
+  const int64_t tiles_m = ceil_div(T, GEMM_SK_BM), tiles_n = ceil_div(c->d_c + c->d_rope, GEMM_SK_BN);
+  if (!bf16 || c->d_model % GEMM_SK_BK != 0 || T < GEMM_SK_BM || tiles_m * tiles_n >= SK_MAX_WGS) return 0;
+  int64_t g = std::min<int64_t>(SK_MAX_WGS / tiles_n, tiles_m * (c->d_model / GEMM_SK_BK) / SK_MIN_SLICES);
+  if (g >= 8) g = g / 8 * 8;
+  return g > tiles_m ? (int)g : 0;
+}
+int kv_parts(const mla_config* c, bool bf16, int64_t T) {
+  const int G = kv_sk_groups(c, bf16, T);
+  if (!G) return 1;
+  const int64_t tiles_m = ceil_div(T, GEMM_SK_BM), nk = c->d_model / GEMM_SK_BK;
+  int p = 1;
+  for (int64_t t = 0; t < tiles_m; ++t) p = std::max(p, gemm_sk_parts(t, nk, tiles_m * nk, G));
+  return p;
 }
 
 struct PrefillWs {
@@ -187,7 +203,7 @@ PrefillWs prefill_layout(const mla_config* c, bool bf16, bool use_explicit, int3
   const int64_t T = (int64_t)B * L, H = c->n_heads, row = c->d_c + c->d_rope;
   const size_t e = bf16 ? 2 : 4;
   p.rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
-  p.kv_raw = (float*)cv.take(kv_ksplit(c, bf16, T) * T * row * 4);
+  p.kv_raw = (float*)cv.take(kv_parts(c, bf16, T) * T * row * 4);
   p.cq_raw = (float*)cv.take(T * c->d_cq * 4);
   p.cq = cv.take(T * c->d_cq * e);
   p.qc = cv.take(T * H * c->d_head * e);
@@ -222,7 +238,7 @@ size_t project_kv_layout(const mla_config* c, bool bf16, int32_t B, int32_t L, v
   Carve cv(ws);
   const int64_t T = (int64_t)B * L;
   *rope_cs = (float*)cv.take((int64_t)L * c->d_rope * 4);
-  *kv_raw = (float*)cv.take(kv_ksplit(c, bf16, T) * T * (c->d_c + c->d_rope) * 4);
+  *kv_raw = (float*)cv.take(kv_parts(c, bf16, T) * T * (c->d_c + c->d_rope) * 4);
   return cv.off;
 }
 
@@ -255,13 +271,25 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
                               float* kv_raw, hipStream_t st) {
   const int64_t T = (int64_t)B * L;
   const int row = c->d_c + c->d_rope;
-  MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, rope_params(c), st));
-  const int ks = kv_ksplit(c, bf16, T), kh = c->d_model / ks;
-  GemmArgs g = gemm(h, c->d_model, kh, w->w_dkv, c->d_model, kh, kv_raw, row, T * row, (int)T, row, kh, ks, false,
+  // with a table (prefill: q^R's RoPE reads it too) the append takes its
+  // angles from it; without, the append forms them itself
+  if (rope_cs) MLA_HIP(launch_rope_table(rope_cs, L, start_pos, c->d_rope, rope_params(c), st));
+  GemmArgs g = gemm(h, c->d_model, 0, w->w_dkv, c->d_model, 0, kv_raw, row, 0, (int)T, row, c->d_model, 1, false,
                     false);
   g.B2 = w->w_kr;
   g.n_split = c->d_c;
-  if (launch_gemm(bf16, g, st) != MLA_OK) return MLA_ERR_HIP;
+  bool sk = false;
+  if (const int G = kv_sk_groups(c, bf16, T)) {
+    g.sk_wgs = G;
+    g.sk_pstride = T * row;
+    const hipError_t e = launch_gemm_bf16_streamk(g, st);
+    if (e == hipSuccess)
+      sk = true;
+    else if (e != hipErrorNotSupported)
+      return MLA_ERR_HIP;
+    g.sk_wgs = 0;
+  }
+  if (!sk && launch_gemm(bf16, g, st) != MLA_OK) return MLA_ERR_HIP;
   AppendArgs a{};
   a.ckv = kv_raw; a.ld_ckv = row;
   a.kr = kv_raw + c->d_c; a.ld_kr = row;
@@ -269,7 +297,9 @@ mla_status project_and_append(const mla_config* c, bool bf16, const mla_kv_cache
   a.seq_idx = nullptr; a.pos = nullptr;
   a.n = (int32_t)T; a.n_seqs = B; a.L = L; a.start_pos = start_pos;
   a.in_f32 = 1;
-  a.part_stride = ks == 2 ? T * row : 0;
+  a.part_stride = sk ? T * row : 0;
+  a.sk_wgs = sk ? kv_sk_groups(c, bf16, T) : 0;
+  a.sk_nk = c->d_model / GEMM_SK_BK;
   a.rope_cs = rope_cs;
   a.pool = k->pool; a.num_pages = k->num_pages;
   a.block_table = k->block_table; a.max_pages = k->max_pages_per_seq; a.page_size = c->page_size;
@@ -420,6 +450,7 @@ mla_status mla_cache_append(const mla_config* cfg, const mla_kv_cache* cache, co
   if (n < 0 || n_seqs <= 0) return MLA_ERR_INVALID_ARG;
   if (n == 0) return MLA_OK;
   if (!ckv_raw || !kr_raw || !g_kv || !seq_idx || !pos) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(ckv_raw) || !aligned16(kr_raw) || !aligned16(g_kv)) return MLA_ERR_INVALID_ARG;
   AppendArgs a{};
   a.ckv = ckv_raw; a.ld_ckv = cfg->d_c;
   a.kr = kr_raw; a.ld_kr = cfg->d_rope;
@@ -462,7 +493,7 @@ mla_status mla_project_kv(const mla_config* cfg, const mla_kv_cache* cache, cons
     return MLA_ERR_OUT_OF_RANGE;
   float *rope_cs, *kv_raw;
   if (project_kv_layout(cfg, bf16, B, L, ws, &rope_cs, &kv_raw) > ws_bytes) return MLA_ERR_WORKSPACE;
-  return project_and_append(cfg, bf16, cache, w, h, B, L, start_pos, rope_cs, kv_raw, (hipStream_t)stream);
+  return project_and_append(cfg, bf16, cache, w, h, B, L, start_pos, nullptr, kv_raw, (hipStream_t)stream);
 }
 
 mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t B, int32_t L, int32_t start_pos,

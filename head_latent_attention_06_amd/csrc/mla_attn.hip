@@ -315,20 +315,33 @@ void attn_bf16_kernel(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t ql = make_rsrc((const bf16*)a.q_lat + hrow * a.ld_q, nh * a.ld_q * 2);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc((const bf16*)a.q_rope + hrow * a.ld_r, nh * a.ld_r * 2);
     const int ol = l32 * a.ld_q * 2 + 16 * hi, orr = l32 * a.ld_r * 2 + 16 * hi;
+    // issued in the order the first tile's MFMAs use them (sched_barrier keeps
+    // the scheduler from reordering), so each MFMA waits only for its own
 #pragma unroll
-    for (int j = 0; j < 32; ++j) qf[j] = buf_ld16(ql, ol + 32 * j);
+    for (int j = 0; j < 32; ++j) {
+      qf[j] = buf_ld16(ql, ol + 32 * j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-    for (int j = 32; j < 36; ++j) qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
+    for (int j = 32; j < 36; ++j) {
+      qf[j] = buf_ld16(qr, orr + 32 * (j - 32));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  // Wait for the queries (and the first tiles) here: left to the compiler, the wait
-  // would sit inside the tile loop in front of the MFMAs that read them and
-  // would drain the tile loads in flight on every pass.
-  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
-               "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]));
-  asm volatile("" ::"v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]), "v"(qf[18]),
-               "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]));
-  asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
-               "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
+  // bf16: the first tile's scores (before the tile loop) read the query
+  // fragments in order, so the compiler's wait for fragment j lets the first
+  // MFMAs start while later fragments are still arriving; those waits precede
+  // the tile loop, which then never waits for the queries (a wait there would
+  // drain the tile loads in flight on every pass).  FP8: the queries are
+  // waited for here, with the staged tiles.
+  if constexpr (FP8) {
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+                 "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]));
+    asm volatile("" ::"v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]), "v"(qf[18]),
+                 "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]));
+    asm volatile("" ::"v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]), "v"(qf[30]),
+                 "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]), "v"(qf[35]));
+  }
   if constexpr (FP8) {
     wait_vmcnt<0>();
     __syncthreads();
@@ -491,7 +504,9 @@ void attn_bf16_kernel(AttnArgs a) {
     flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
   };
   f32x16 s_nx;  // scores of the next tile
-  // (tiles 0 .. DEPTH-1 have landed with the queries)
+  // bf16: tile 0 has landed once at most tiles 1 .. DEPTH-1 and the 36 query
+  // loads are outstanding (loads complete in order); FP8: everything has
+  if constexpr (!FP8) wait_vmcnt<(DEPTH - 1) * DMA_PER_THREAD + 36>();
   __syncthreads();
   {
     const unsigned char* K0 = smem;

@@ -210,12 +210,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // 16-byte fragment read from LDS feeds several MFMAs (an A fragment BN/64, a B
 // fragment 4).  K moves in slices of 32 through a ring of four LDS stages
 // filled by direct-to-LDS buffer loads (three slices in flight).  Each 64-byte
-// tile row keeps its four 16-byte chunks at chunk ^ ((row >> 1) & 3), which
-// keeps the fragment reads free of bank conflicts; the loads apply the
-// permutation on the global side.  The product is formed transposed
+// tile row keeps its four 16-byte chunks at chunk ^ ((row >> 2) & 3): a
+// 16-byte fragment read serves 16 lanes (16 consecutive tile rows, one chunk
+// each) per pass over the LDS's 64 four-byte banks, and rows r, r + 4, r + 8,
+// r + 12 share a bank group unless their chunks differ, which this
+// permutation makes them do (with (row >> 1) & 3 rows r and r + 8 collided:
+// bank-conflict stalls of 8-14 % of the kernel time were counted).  The loads
+// apply the permutation on the global side.  The product is formed transposed
 // (C^T = B A^T) so each lane holds four consecutive output columns; the output
 // goes through LDS so that every store writes whole rows.
 constexpr int GB_BM = 256, GB_BK = 32, GB_NST = 4, GB_GM = 4;
+constexpr int GB_SK_BN = 192;  // column tile of the stream-K form
 constexpr int GB_ROW = GB_BK * 2;  // bytes per tile row
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at lds_addr + 16 * lane
@@ -240,7 +245,7 @@ __device__ __forceinline__ const T* gb_uniform(const T* p) {
   return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int BN, bool OUT_BF16, bool ROPE = false>
+template <int BN, bool OUT_BF16, bool ROPE = false, bool SK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_big_kernel(GemmArgs g) {
   constexpr int A_BYTES = GB_BM * GB_ROW, B_BYTES = BN * GB_ROW, STG = A_BYTES + B_BYTES;
@@ -254,30 +259,72 @@ void gemm_big_kernel(GemmArgs g) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Tile order: consecutive ids run on one XCD (xcd_remap); within a group of
-  // GB_GM row tiles the column tile advances every GB_GM ids, so the ~32
-  // workgroups an XCD runs at once cover about 4 x 8 tiles and share their
-  // A and B slices in that XCD's L2.
   const int tiles_n = (g.N + BN - 1) / BN, tiles_m = (g.M + GB_BM - 1) / GB_BM;
-  const int r = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int group = r / (GB_GM * tiles_n), first_m = group * GB_GM;
-  const int gsz = min(GB_GM, tiles_m - first_m), idx = r - group * GB_GM * tiles_n;
-  const int tm = first_m + idx % gsz, tn = idx / gsz;
-  const int z = blockIdx.y;
+  const int nk = g.K / GB_BK;
+  const int64_t lda2 = g.lda * 2, ldb2 = g.ldb * 2;
+  // Load i of wave w moves tile rows 16 (4 i + w) .. +15 (64 bytes each):
+  // lane l writes LDS bytes 16 l of that 1 KB, i.e. row + l/4, slot l%4,
+  // holding the row's logical chunk (l%4) ^ ((l/16) & 3).
+  const int32_t va = (int32_t)((lane >> 2) * lda2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+  const int32_t vb = (int32_t)((lane >> 2) * ldb2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  // Fragment of tile row R (lane l32), k step ks: bytes R*64 + 16 ((2 ks + hi) ^ ((R >> 2) & 3))
+  // = (R*64 + 16 (hi ^ ((R >> 2) & 3))) ^ 32 ks.
+  const int ra = wm * 128 + l32, rb = wn * (BN / 2) + l32;
+  const uint32_t fa = ra * GB_ROW + 16 * (hi ^ ((ra >> 2) & 3));            // + 32 mi rows: same XOR term
+  const uint32_t fb = A_BYTES + rb * GB_ROW + 16 * (hi ^ ((rb >> 2) & 3));  // + 32 ni rows likewise
+  u32x4 af[2][4], bfr[2][TN];
+  f32x16 acc[4][TN];  // [m tuple][n tuple], C^T layout
+
+  // Work of this workgroup.  Tile order: consecutive ids run on one XCD
+  // (xcd_remap); within a group of GB_GM row tiles the column tile advances
+  // every GB_GM ids, so the ~32 workgroups an XCD runs at once cover about
+  // 4 x 8 tiles and share their A and B slices in that XCD's L2.
+  // Stream-K (SK, batch 1): groups of tiles_n workgroups with consecutive ids
+  // (so on one XCD, together) each take one column tile of the same rows; the
+  // (row tile, k slice) units, k fastest, are cut into sk_wgs equal runs of
+  // consecutive units, one per group.  A run covers the end of one row tile
+  // and the start of the next (or more); each piece ("segment") writes fp32
+  // partial sums of its tile to partial buffer p = this run's index minus
+  // that of the run holding the row tile's first slice (sk_pstride elements
+  // apart), and the consumer adds a row tile's partials (gemm_sk_parts).
+  // The tiles_n workgroups of a group read the same rows of A at the same k,
+  // so A comes from HBM about once.
+  constexpr bool sk = SK;
+  const int wgid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int64_t U = (int64_t)tiles_m * nk, G = g.sk_wgs;
+  const int grp = wgid / tiles_n;
+  int64_t u = sk && grp < G ? (int64_t)grp * U / G : 0;
+  const int64_t u_end = sk && grp < G ? (int64_t)(grp + 1) * U / G : 0;
+  for (int seg = 0;; ++seg) {
+  int tm, tn, ka, kend;
+  int64_t coff;  // element offset of this segment's output
+  if (sk) {
+    if (u >= u_end) break;
+    tm = (int)(u / nk);
+    tn = wgid % tiles_n;
+    ka = (int)(u % nk);
+    kend = (int)min<int64_t>(nk, ka + (u_end - u));
+    const int64_t first = (((int64_t)tm * nk + 1) * G - 1) / U;  // run holding the row tile's slice 0
+    coff = (grp - first) * g.sk_pstride;
+    u += kend - ka;
+  } else {
+    if (seg) break;
+    const int group = wgid / (GB_GM * tiles_n), first_m = group * GB_GM;
+    const int gsz = min(GB_GM, tiles_m - first_m), idx = wgid - group * GB_GM * tiles_n;
+    tm = first_m + idx % gsz;
+    tn = idx / gsz;
+    ka = 0;
+    kend = nk;
+    coff = (int64_t)blockIdx.y * g.strideC;
+  }
+  const int ns = kend - ka;  // slices of this segment
+  const int z = sk ? 0 : (int)blockIdx.y;
   const int m0 = tm * GB_BM, n0 = tn * BN;
   const unsigned char* A = (const unsigned char*)g.A + (int64_t)z * g.strideA * 2;
   const unsigned char* B = (const unsigned char*)g.B + (int64_t)z * g.strideB * 2;
-  const int64_t lda2 = g.lda * 2, ldb2 = g.ldb * 2;
-
-  // Load i of wave w moves tile rows 16 (4 i + w) .. +15 (64 bytes each):
-  // lane l writes LDS bytes 16 l of that 1 KB, i.e. row + l/4, slot l%4,
-  // holding the row's logical chunk (l%4) ^ ((l/8) & 3).
-  const int32_t va = (int32_t)((lane >> 2) * lda2) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
-  const int32_t vb = (int32_t)((lane >> 2) * ldb2) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
-  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
-  const int nk = g.K / GB_BK;
-  // One buffer resource per load, built once: rows past M (or N) lie outside
-  // it and load as zero; the slice's k offset goes in the scalar offset.
+  // One buffer resource per load, built once per tile: rows past M (or N) lie
+  // outside it and load as zero; the slice's k offset goes in the scalar offset.
   __amdgpu_buffer_rsrc_t rsa[NA], rsb[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -307,7 +354,7 @@ void gemm_big_kernel(GemmArgs g) {
   // so every slice issues the same loads and the vmcnt bookkeeping stays uniform)
   // load n (< NA: A rows, else B rows) of slice kt
   auto issue_one = [&](int kt, int n) {
-    const int32_t kb = __builtin_amdgcn_readfirstlane(min(kt, nk - 1) * GB_BK * 2);
+    const int32_t kb = __builtin_amdgcn_readfirstlane((ka + min(kt, ns - 1)) * GB_BK * 2);
     const uint32_t st = sbase + (kt % GB_NST) * STG;
     if (n < NA)
       gb_dma16(rsa[n], st + 16 * (4 * n + wave) * GB_ROW, va, kb);
@@ -319,12 +366,6 @@ void gemm_big_kernel(GemmArgs g) {
     for (int n = 0; n < NLD; ++n) issue_one(kt, n);
   };
 
-  // Fragment of tile row R (lane l32), k step ks: bytes R*64 + 16 ((2 ks + hi) ^ ((R >> 1) & 3))
-  // = (R*64 + 16 (hi ^ ((R >> 1) & 3))) ^ 32 ks.
-  const int ra = wm * 128 + l32, rb = wn * (BN / 2) + l32;
-  const uint32_t fa = ra * GB_ROW + 16 * (hi ^ ((ra >> 1) & 3));            // + 32 mi rows: same XOR term
-  const uint32_t fb = A_BYTES + rb * GB_ROW + 16 * (hi ^ ((rb >> 1) & 3));  // + 32 ni rows likewise
-  u32x4 af[2][4], bfr[2][TN];
   auto load_frags = [&](int set, int kt, int ks) {
     const uint32_t st = sbase + (kt % GB_NST) * STG;
 #pragma unroll
@@ -333,7 +374,6 @@ void gemm_big_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) bfr[set][j] = gb_lds16((st + fb + j * 32 * GB_ROW) ^ (32 * ks));
   };
 
-  f32x16 acc[4][TN];  // [m tuple][n tuple], C^T layout
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -361,7 +401,7 @@ void gemm_big_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);  // keep the MFMA / load interleave as written
       }
   };
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < ns; ++kt) {
     const uint32_t st = sbase + (kt % GB_NST) * STG;
     // k step 0, reading k step 1's fragments
     kstep(0, [&](int i, int j) {
@@ -393,24 +433,25 @@ void gemm_big_kernel(GemmArgs g) {
   // Output through LDS, one wave's 128 x BN/2 block at a time per wave-private
   // quarter of the stage memory, so every store instruction writes whole rows: lane (l32, hi)
   // of acc[i][j] holds row 32 i + l32, columns 32 j + 8 q + 4 hi .. +3 (register
-  // 4 q + e).  The block goes through in passes of PR rows; 16-byte chunk c of
-  // a staged row sits at c ^ (row % CPR) (CPR chunks per row), which keeps the
-  // writes (one row per lane) and the row-contiguous reads free of conflicts;
-  // rows of 12 or 24 chunks (192 columns) rotate by the row instead.
+  // 4 q + e).  The block goes through in passes of PR rows.  Rows of 16 or 32
+  // chunks (256 columns) keep 16-byte chunk c at c ^ (row % CPR); rows of 12
+  // or 24 chunks (192 columns) are staged with one spare chunk per row (an
+  // odd stride in chunks), so the 16 rows one write pass covers fall in 16
+  // different bank groups with no permutation.
   __syncthreads();  // every wave is done with the k-slice stages
   constexpr int ES = OUT_BF16 ? 2 : 4;                 // output element bytes
-  constexpr int RB = (BN / 2) * ES;                    // staged row bytes (256 / 192 or 512 / 384)
-  constexpr int CPR = RB / 16;                         // chunks per row
-  constexpr int PR = 32768 / RB >= 128 ? 128 : 64;     // rows per pass (whole 32-row tuples)
+  constexpr int CPR = (BN / 2) * ES / 16;              // chunks per row (16 / 12 or 32 / 24)
   constexpr bool POW2 = (CPR & (CPR - 1)) == 0;
+  constexpr int RB = (CPR + (POW2 ? 0 : 1)) * 16;      // staged row stride in bytes
+  constexpr int PR = 32768 / RB >= 128 ? 128 : 64;     // rows per pass (whole 32-row tuples)
   // staged position of chunk c of row r, and its inverse
-  const auto perm = [](int c, int r) { return POW2 ? c ^ (r & (CPR - 1)) : (c + r) % CPR; };
-  const auto iperm = [](int p, int r) { return POW2 ? p ^ (r & (CPR - 1)) : (p + CPR - r % CPR) % CPR; };
+  const auto perm = [](int c, int r) { return POW2 ? c ^ (r & (CPR - 1)) : c; };
+  const auto iperm = [](int p, int r) { return POW2 ? p ^ (r & (CPR - 1)) : p; };
   constexpr int EREG = GB_NST * STG / 4;  // each wave's share of the stage memory
   static_assert(PR * RB <= EREG, "staging pass exceeds the wave's LDS share");
   const uint32_t ew = sbase + wave * EREG;
   const int col0 = n0 + (BN / 2) * wn;
-  unsigned char* cbase = (unsigned char*)g.C + (int64_t)z * g.strideC * ES;
+  unsigned char* cbase = (unsigned char*)g.C + coff * ES;
 #pragma unroll
   for (int pass = 0; pass < 128 / PR; ++pass) {
 #pragma unroll
@@ -446,18 +487,23 @@ void gemm_big_kernel(GemmArgs g) {
         }
     }
     // (a wave reads back only its own writes: LDS ops of one wave complete in order)
-    // lane l reads chunk position l % CPR of staged row l / CPR (+ 64 / CPR per
-    // step; with 12 or 24 chunks per row the last 4 or 16 lanes idle)
-    constexpr int RSTEP = 64 / CPR;  // rows per read instruction
+    // A row takes LPR lanes (CPR rounded up to whole 16-lane passes): lane l
+    // reads chunk position l % LPR of staged row l / LPR, so each pass reads
+    // contiguous bytes of one row; with 12 or 24 chunks per row 4 or 8 lanes
+    // of each row's last pass idle
+    constexpr int LPR = (CPR + 15) / 16 * 16;
+    constexpr int RSTEP = 64 / LPR;  // rows per read instruction
 #pragma unroll 4
     for (int rr = 0; rr < PR; rr += RSTEP) {
-      const int r = rr + lane / CPR, pos = lane % CPR;
-      if (lane >= CPR * RSTEP || r >= PR) continue;
+      const int r = rr + lane / LPR, pos = lane % LPR;
+      if (pos >= CPR || r >= PR) continue;
       const u32x4 v = gb_lds16(ew + r * RB + pos * 16);
       const int row = m0 + 128 * wm + pass * PR + r;
       const int col = col0 + (iperm(pos, r) * 16) / ES;
       if (row < g.M && col < g.N) *reinterpret_cast<u32x4*>(cbase + ((int64_t)row * g.ldc + col) * ES) = v;
     }
+  }
+  __syncthreads();  // every wave has read back its staging before the next segment's loads
   }
 }
 
@@ -695,6 +741,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
     else
       hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, dim3(256), 0, st, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_streamk(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.batch != 1 || g.out_bf16 || g.sk_wgs <= 0 || !bigtile_form(g)) return hipErrorNotSupported;
+  const unsigned wgs = (unsigned)(g.sk_wgs * ((g.N + GB_SK_BN - 1) / GB_SK_BN));
+  hipLaunchKernelGGL((gemm_big_kernel<GB_SK_BN, false, false, true>), dim3(wgs), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -72,9 +72,28 @@ struct GemmArgs {
   // n % rope_d of a head, row m takes position row rope_cs row m % rope_rows
   // ([rows, rope_d/2, 2] cos/sin), interleaved pairs (2p, 2p+1)
   const float* rope_cs; int32_t rope_rows, rope_d;
+  // stream-K form (launch_gemm_bf16_streamk): sk_wgs groups of workgroups
+  // (one per GEMM_SK_BN column tile) share the (row tile, k slice) units of
+  // GEMM_SK_BM-row tiles equally; partial p of a row tile goes to
+  // C + p * sk_pstride (see gemm_sk_parts)
+  int32_t sk_wgs; int64_t sk_pstride;
 };
 
+constexpr int GEMM_SK_BM = 256, GEMM_SK_BN = 192, GEMM_SK_BK = 32;
+
+// Partial sums of row tile t of a stream-K product with U = row tiles *
+// slices units over W groups: the runs holding the tile's first and last
+// slice, and every run between, each wrote one partial.
+__host__ __device__ inline int gemm_sk_parts(int64_t t, int64_t slices, int64_t U, int64_t W) {
+  const int64_t first = ((t * slices + 1) * W - 1) / U;
+  const int64_t last = ((t * slices + slices) * W - 1) / U;
+  return (int)(last - first + 1);
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+// The stream-K form (fp32 output, batch 1); hipErrorNotSupported for shapes
+// the large-tile kernel does not take.
+hipError_t launch_gemm_bf16_streamk(const GemmArgs& g, hipStream_t st);
 // The GEMM with RoPE applied to its bf16 output in the same kernel; returns
 // hipErrorNotSupported (launching nothing) for shapes the fused form does not
 // take, so the caller can run the GEMM and the rotation separately.
@@ -109,8 +128,10 @@ struct AppendArgs {
   const int32_t* seq_idx; const int32_t* pos;
   int32_t n, n_seqs, L, start_pos;
   int32_t in_f32;                    // ckv / kr are fp32 (else cfg dtype)
-  int64_t part_stride;               // in_f32: each value is the sum of two partial products, the second
-                                     // part_stride elements after the first (0: one product)
+  int64_t part_stride;               // in_f32 with sk_wgs > 0: each value is the sum of the partial
+                                     // products of a stream-K GEMM (part_stride elements apart) over
+                                     // sk_wgs groups and sk_nk k slices (gemm_sk_parts); 0: one product
+  int32_t sk_wgs, sk_nk;
   const float* rope_cs;              // optional [L, d_rope/2, 2] cos/sin for implicit positions
   void* pool; int64_t num_pages;
   const int32_t* block_table; int32_t max_pages, page_size;

@@ -45,6 +45,15 @@ __device__ __forceinline__ float ld_as_f32(const void* p, int64_t i) {
   return to_f32(((const T*)p)[i]);
 }
 
+// Partial products that make up input column col of token i: one, or those
+// of a stream-K product (part_stride elements apart).
+__device__ __forceinline__ int n_parts(const AppendArgs& a, int i, int col) {
+  (void)col;  // every column tile of a row tile has the same partials
+  if (!a.part_stride || !a.sk_wgs) return 1;
+  const int64_t U = (int64_t)((a.n + GEMM_SK_BM - 1) / GEMM_SK_BM) * a.sk_nk;
+  return gemm_sk_parts(i / GEMM_SK_BM, a.sk_nk, U, a.sk_wgs);
+}
+
 // One wave per appended token.
 template <typename TIN, typename TOUT>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
@@ -75,23 +84,25 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int row = a.d_c + a.d_rope;
   TOUT* dst = (TOUT*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * row;
   const int64_t ci = (int64_t)i * a.ld_ckv, ki = (int64_t)i * a.ld_kr;
-  // the projection, as one product or the sum of its two k-halves
-  const auto in = [&](const void* p, int64_t o) {
+  // the projection, as one product or the sum of its partial products
+  // (column col of the product: latent dims, then the d_rope of k^R)
+  const auto in = [&](const void* p, int64_t o, int col) {
     float x = ld_as_f32<TIN>(p, o);
-    if (a.part_stride) x += ld_as_f32<TIN>(p, o + a.part_stride);
+    const int np = n_parts(a, i, col);
+    for (int q = 1; q < np; ++q) x += ld_as_f32<TIN>(p, o + q * a.part_stride);
     return x;
   };
 
   // RMSNorm of the latent
   float ss = 0.f;
   for (int d = lane; d < a.d_c; d += 64) {
-    const float x = in(a.ckv, ci + d);
+    const float x = in(a.ckv, ci + d, d);
     ss += x * x;
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)a.d_c + a.eps);
   for (int d = lane; d < a.d_c; d += 64) {
-    const float x = in(a.ckv, ci + d);
+    const float x = in(a.ckv, ci + d, d);
     const float g = ld_as_f32<TOUT>(a.g_kv, d);
     dst[d] = from_f32<TOUT>(x * inv * g);
   }
@@ -105,9 +116,114 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     } else {
       rope_cos_sin(pos, p, a.d_rope, a.rope, c, s);
     }
-    const float x0 = in(a.kr, ki + 2 * p), x1 = in(a.kr, ki + 2 * p + 1);
+    const float x0 = in(a.kr, ki + 2 * p, a.d_c + 2 * p), x1 = in(a.kr, ki + 2 * p + 1, a.d_c + 2 * p + 1);
     dst[a.d_c + 2 * p] = from_f32<TOUT>(c * x0 - s * x1);
     dst[a.d_c + 2 * p + 1] = from_f32<TOUT>(s * x0 + c * x1);
+  }
+}
+
+// The same for a bf16 cache with the V3 widths (d_c = 512, d_rope = 64),
+// four tokens per workgroup (one per wave) and 16-byte accesses: lane l
+// holds dims 8l .. 8l+7 of the latent (two 16-byte loads of fp32 input per
+// partial, one of bf16 input) and writes them with one 16-byte store; lanes
+// 0 .. 31 rotate pair l of k^R.
+template <typename TIN>
+__device__ __forceinline__ void load8(const void* p, int64_t o, float (&y)[8]) {
+  if constexpr (sizeof(TIN) == 4) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>((const float*)p + o);
+    const f32x4 v = *reinterpret_cast<const f32x4*>((const float*)p + o + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[k] = u[k];
+      y[4 + k] = v[k];
+    }
+  } else {
+    const u32x4 u = *reinterpret_cast<const u32x4*>((const bf16*)p + o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[2 * k] = bf16_lo(u[k]);
+      y[2 * k + 1] = bf16_hi(u[k]);
+    }
+  }
+}
+template <typename TIN>
+__global__ __launch_bounds__(256) void append_bf16_v3_kernel(AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= a.n) return;
+  int b, pos;
+  if (a.seq_idx) {
+    b = a.seq_idx[i];
+    pos = a.pos[i];
+  } else {
+    b = i / a.L;
+    pos = a.start_pos + i % a.L;
+  }
+  if (b < 0 || b >= a.n_seqs) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_SEQ);
+    return;
+  }
+  const int pidx = pos >= 0 ? pos / a.page_size : -1;
+  if (pidx < 0 || pidx >= a.max_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_POS);
+    return;
+  }
+  const int page = a.block_table[(int64_t)b * a.max_pages + pidx];
+  if (page < 0 || (int64_t)page >= a.num_pages) {
+    if (lane == 0 && a.err_flags) atomicOr(a.err_flags, FLAG_BAD_PAGE);
+    return;
+  }
+  bf16* dst = (bf16*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * 576;
+  const int64_t ci = (int64_t)i * a.ld_ckv + 8 * lane, ki = (int64_t)i * a.ld_kr;
+  // RMSNorm of the latent (the projection, or the sum of its partial products)
+  float y[8];
+  load8<TIN>(a.ckv, ci, y);
+  const int np = n_parts(a, i, 8 * lane);
+  for (int q = 1; q < np; ++q) {
+    float z[8];
+    load8<TIN>(a.ckv, ci + q * a.part_stride, z);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] += z[k];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += y[k] * y[k];
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / 512.f + a.eps);
+  const u32x4 g = *reinterpret_cast<const u32x4*>((const bf16*)a.g_kv + 8 * lane);
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = pack_bf16x2(y[2 * k] * inv * bf16_lo(g[k]), y[2 * k + 1] * inv * bf16_hi(g[k]));
+  *reinterpret_cast<u32x4*>(dst + 8 * lane) = o;
+  // RoPE of the shared decoupled key
+  if (lane < 32) {
+    const int p = lane;
+    float c, s;
+    if (a.rope_cs) {
+      const float* cs = a.rope_cs + ((int64_t)(i % a.L) * 32 + p) * 2;
+      c = cs[0];
+      s = cs[1];
+    } else {
+      rope_cos_sin(pos, p, 64, a.rope, c, s);
+    }
+    float x0, x1;
+    if constexpr (sizeof(TIN) == 4) {
+      const float2 v = *reinterpret_cast<const float2*>((const float*)a.kr + ki + 2 * p);
+      x0 = v.x;
+      x1 = v.y;
+      const int npr = n_parts(a, i, 512 + 2 * p);
+      for (int q = 1; q < npr; ++q) {
+        const float2 w = *reinterpret_cast<const float2*>((const float*)a.kr + ki + q * a.part_stride + 2 * p);
+        x0 += w.x;
+        x1 += w.y;
+      }
+    } else {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>((const bf16*)a.kr + ki + 2 * p);
+      x0 = bf16_lo(v);
+      x1 = bf16_hi(v);
+    }
+    *reinterpret_cast<uint32_t*>(dst + 512 + 2 * p) = pack_bf16x2(c * x0 - s * x1, s * x0 + c * x1);
   }
 }
 
@@ -147,9 +263,10 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(AppendArgs a) {
   }
   unsigned char* dst = (unsigned char*)a.pool + ((int64_t)page * a.page_size + pos % a.page_size) * FP8_ROW;
   const int64_t ci = (int64_t)i * a.ld_ckv, ki = (int64_t)i * a.ld_kr;
-  const auto in = [&](const void* p, int64_t o) {
+  const auto in = [&](const void* p, int64_t o, int col) {  // col: column of the projection
     float x = ld_as_f32<TIN>(p, o);
-    if (a.part_stride) x += ld_as_f32<TIN>(p, o + a.part_stride);
+    const int np = n_parts(a, i, col);
+    for (int q = 1; q < np; ++q) x += ld_as_f32<TIN>(p, o + q * a.part_stride);
     return x;
   };
   // RMSNorm of the latent (d_c = 512)
@@ -157,7 +274,7 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(AppendArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    y[k] = in(a.ckv, ci + 8 * lane + k);
+    y[k] = in(a.ckv, ci + 8 * lane + k, 8 * lane + k);
     ss += y[k] * y[k];
   }
   ss = wave_sum(ss);
@@ -194,7 +311,7 @@ __global__ __launch_bounds__(64) void append_fp8_kernel(AppendArgs a) {
     } else {
       rope_cos_sin(pos, p, 64, a.rope, c, s);
     }
-    const float x0 = in(a.kr, ki + 2 * p), x1 = in(a.kr, ki + 2 * p + 1);
+    const float x0 = in(a.kr, ki + 2 * p, 512 + 2 * p), x1 = in(a.kr, ki + 2 * p + 1, 513 + 2 * p);
     *reinterpret_cast<uint32_t*>(dst + FP8_KR + 4 * p) = pack_bf16x2(c * x0 - s * x1, s * x0 + c * x1);
   }
 }
@@ -287,6 +404,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((append_fp8_kernel<float>), grid, block, 0, st, a);
     else
       hipLaunchKernelGGL((append_fp8_kernel<bf16>), grid, block, 0, st, a);
+  } else if (a.bf16_cache && a.d_c == 512 && a.d_rope == 64) {
+    const dim3 g4((unsigned)((a.n + 3) / 4)), b4(256);
+    if (a.in_f32)
+      hipLaunchKernelGGL((append_bf16_v3_kernel<float>), g4, b4, 0, st, a);
+    else
+      hipLaunchKernelGGL((append_bf16_v3_kernel<bf16>), g4, b4, 0, st, a);
   } else if (a.bf16_cache) {
     if (a.in_f32)
       hipLaunchKernelGGL((append_kernel<float, bf16>), grid, block, 0, st, a);

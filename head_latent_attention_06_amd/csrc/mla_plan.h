@@ -98,26 +98,48 @@ __device__ inline void plan_body(const AttnArgs& a, int32_t* plan, int32_t targe
   }
   // Per-workgroup item table in launch order (each thread re-reads only the
   // row offsets it wrote itself).  Workgroup i runs on XCD i % 8.  Without
-  // longest_first the items go to the XCDs in 8 runs of consecutive items, so
-  // the chunks of one row (which read the same queries) share an L2; with
-  // longest_first the items run in reverse plan order.  The grid has at least
-  // n_items + 7 slots.
+  // longest_first the items go to the XCDs in 8 runs of consecutive launch
+  // ordinals, so the chunks of one row (which read the same queries) share an
+  // L2; with longest_first the items run in reverse plan order.  The grid has
+  // at least n_items + 7 slots.
+  // Launch ordinals: the plan order, except that with a few query rows per
+  // sequence (s_q <= MAX_COSCHED) chunk i of every row of a sequence are
+  // neighbours: they read the same cache pages, so running them at the same
+  // time on one XCD lets the L2 serve the second read of each tile.
+  constexpr int MAX_COSCHED = 8;
   const int n_items = carry;
   const int per = (n_items + 7) / 8;
+  const bool cosched = !a.longest_first && a.s_q > 1 && a.s_q <= MAX_COSCHED;
   int4* info = reinterpret_cast<int4*>(plan + plan_info_offset(n_rows));
   for (int r = tid; r < n_rows; r += 256) {
     const int v = vis(r, false);
     const int c = (v + chunk - 1) / chunk;
     const int first = plan[2 + r];
+    int cs[MAX_COSCHED];
+    int seq_first = first;  // the sequence's first item (its rows' items are contiguous)
+    const int s = r % a.s_q, rb = r - s;
+    if (cosched) {
+#pragma unroll
+      for (int s2 = 0; s2 < MAX_COSCHED; ++s2) {
+        cs[s2] = s2 < a.s_q ? (vis(rb + s2, false) + chunk - 1) / chunk : 0;
+        if (s2 < s) seq_first -= cs[s2];
+      }
+    }
     for (int i = 0; i < c; ++i) {
       const int item = first + i;
-      const int slot = a.longest_first ? n_items - 1 - item : (item % per) * 8 + item / per;
+      int ord = item;
+      if (cosched) {  // items of the sequence with a lower chunk index, then this chunk's earlier rows
+        ord = seq_first;
+#pragma unroll
+        for (int s2 = 0; s2 < MAX_COSCHED; ++s2) ord += min(cs[s2], i) + (s2 < s && cs[s2] > i ? 1 : 0);
+      }
+      const int slot = a.longest_first ? n_items - 1 - item : (ord % per) * 8 + ord / per;
       info[slot] = make_int4(r, i * chunk, min((i + 1) * chunk, v), (item << 1) | (c > 1 ? 1 : 0));
     }
   }
-  for (int s2 = tid; s2 < a.max_items; s2 += 256) {
-    const bool used = a.longest_first ? s2 < n_items : (s2 / 8 < per && (s2 % 8) * per + s2 / 8 < n_items);
-    if (!used) info[s2] = make_int4(0, 0, 0, 0);
+  for (int s3 = tid; s3 < a.max_items; s3 += 256) {
+    const bool used = a.longest_first ? s3 < n_items : (s3 / 8 < per && (s3 % 8) * per + s3 / 8 < n_items);
+    if (!used) info[s3] = make_int4(0, 0, 0, 0);
   }
 }
 

@@ -328,11 +328,13 @@ def test_fp8_decode_hip_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("L", [10752, 10753])
-def test_fp8_project_kv_both_sides_of_the_k_split(L):
-    """[W^DKV ; W^KR] h then the FP8 append, at the last token count whose
-    projection runs as two k-halves summed by the append (10752) and the first
-    that runs as one (10753); sampled rows against the oracle's FP8 rows."""
+@pytest.mark.parametrize("L", [300, 20224, 20225])
+def test_fp8_project_kv_both_sides_of_the_stream_k_form(L):
+    """[W^DKV ; W^KR] h then the FP8 append, where the projection runs in the
+    stream-K form and the append adds its partial sums (300 and 20,224
+    tokens, the last count with fewer 256-row tiles than stream-K groups) and
+    where it runs as one plain launch (20,225); sampled rows against the
+    oracle's FP8 rows."""
     shape = S
     cfg = _cfg(shape)
     w = mi.weights(117, shape)
@@ -344,7 +346,7 @@ def test_fp8_project_kv_both_sides_of_the_k_split(L):
     torch.cuda.synchronize()
     assert int(cache.err_flags.item()) == 0
     pool = cache.pool.cpu().numpy()
-    toks = np.unique(np.array([0, 1, 255, 256, 4095, L // 2, L - 257, L - 256, L - 2, L - 1]))
+    toks = np.unique(np.array([0, 1, 255, 256, 4095, L // 2, L - 257, L - 256, L - 2, L - 1]) % L)
     c, kr = om.latent_rows(h[0][toks], w["w_dkv"], w["g_kv"], w["w_kr"], toks, shape.rms_eps, shape.rope_base)
     ref = np.concatenate([om.quantize_latent_fp8(c)[2], kr], axis=1)
     got = _deq(np.stack([pool[om.paged_slot(bt, 0, int(t), shape.page_size)] for t in toks]))

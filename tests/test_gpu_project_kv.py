@@ -51,12 +51,15 @@ def test_project_kv_f32_tiny():
         assert rel_l2(rows, np.concatenate([c, kr], 1)) <= F32_TOL
 
 
-@pytest.mark.parametrize("B,L", [(2, 4096), (1, 10752), (1, 10753)])
+@pytest.mark.parametrize("B,L", [(1, 255), (1, 300), (2, 4096), (1, 20224), (1, 20225)])
 def test_project_kv_bf16_large(B, L):
-    """Token counts that take the 256-row GEMM tiles: up to 10752 tokens the
-    reduction over d_model runs as two halves summed by the append, from
-    10753 on as one (the boundary sits on both sides); sampled rows include
-    tile edges and the ragged last tile."""
+    """Token counts around the forms of the down-projection GEMM: below 256
+    tokens the 128 x 128 kernel; from 256 tokens while there are fewer row
+    tiles of 256 than the 80 workgroup groups of the stream-K form (up to
+    20,224 tokens) that form, whose partial sums the append adds (300 tokens:
+    8 groups, up to four partials per row tile; 8192: 80 groups, up to
+    three); past that one plain launch (20,225).  Sampled rows include tile
+    edges and the ragged last tile."""
     s = mi.V3
     cfg = config(s)
     w = mi.weights(53, s)
