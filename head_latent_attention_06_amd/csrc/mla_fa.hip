@@ -177,30 +177,34 @@ void fa_bf16_kernel(FaArgs a) {
   const int64_t krow_bytes = (int64_t)H * FA_DH * 2;
   // Instruction i of wave w moves rows 4 (4i + w) .. +3 (k^C, v^C: 16 chunks
   // per row) or 8 (4i + w) .. +7 (k^R: 8 chunks); the swizzle of those rows
-  // depends on the lane only, so one per-lane offset per source serves every
-  // instruction and the row group is folded into the buffer resource.
+  // depends on the lane only.  Each load's per-lane offset (its rows and the
+  // lane's swizzled chunk) is fixed for the whole kernel, so a tile needs one
+  // buffer resource per source, bounded by its valid rows (rows past the end
+  // are outside it and load as zero), and a load costs an M0 write and the
+  // load itself.
   const int ldkr2 = a.ld_kr * 2;
   const int32_t dkc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * wave + (lane >> 4)));
   const int32_t dvc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
   const int32_t dkr = (lane >> 3) * ldkr2 + 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
+  int32_t voff[FA_DMA];  // n < 8: k^C (n even) / v^C (n odd) rows 4 (4 (n/2) + w) ..; n >= 8: k^R rows 8 (4 (n-8) + w) ..
+#pragma unroll
+  for (int n = 0; n < FA_DMA; ++n)
+    voff[n] = n < 8 ? (int32_t)(4 * (4 * (n >> 1) + wave) * krow_bytes) + ((n & 1) ? dvc : dkc)
+                    : 8 * (4 * (n - 8) + wave) * ldkr2 + dkr;
   const int64_t key_base = (int64_t)b * a.kv_end;
-  // Sources of tile t (possibly past the end: empty resources) and its ten
-  // 16-byte-per-lane loads: n < 8 k^C / v^C rows 4 (4 (n/2) + w) .., n >= 8
-  // k^R rows 8 (4 (n-8) + w) ..
   struct TileSrc {
-    const unsigned char *kc, *vc, *kr;
-    int32_t nb_kv, nb_r;
+    __amdgpu_buffer_rsrc_t rk, rv, rr;
     uint32_t ks, vs;
   };
   auto tile_src = [&](int t) {
     const int kb0 = t * FA_KT;
     const int rows = max(0, min(FA_KT, kv_hi - kb0));
     TileSrc ts;
-    ts.kc = fa_uniform((const unsigned char*)a.kc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2);
-    ts.vc = fa_uniform((const unsigned char*)a.vc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2);
-    ts.kr = fa_uniform((const unsigned char*)a.kr + (key_base + kb0) * ldkr2);
-    ts.nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
-    ts.nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
+    const int32_t nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
+    const int32_t nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
+    ts.rk = fa_rsrc(fa_uniform((const unsigned char*)a.kc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
+    ts.rv = fa_rsrc(fa_uniform((const unsigned char*)a.vc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
+    ts.rr = fa_rsrc(fa_uniform((const unsigned char*)a.kr + (key_base + kb0) * ldkr2), nb_r);
     ts.ks = __builtin_amdgcn_readfirstlane(smem_addr + (t % FA_NK) * FA_KSTAGE);
     ts.vs = __builtin_amdgcn_readfirstlane(smem_addr + FA_VBASE + (t % FA_NV) * FA_VSTAGE);
     return ts;
@@ -208,16 +212,12 @@ void fa_bf16_kernel(FaArgs a) {
   auto dma_one = [&](const TileSrc& ts, int n) {
     if (n < 8) {
       const int i = n >> 1;
-      const int32_t u = __builtin_amdgcn_readfirstlane((int32_t)(4 * (4 * i + wave) * krow_bytes));
-      const int32_t nb = max(0, ts.nb_kv - u);
       if (n & 1)
-        fa_dma16(fa_rsrc(fa_uniform(ts.vc + u), nb), ts.vs + (4 * i + wave) * 1024, dvc);
+        fa_dma16(ts.rv, ts.vs + (4 * i + wave) * 1024, voff[n]);
       else
-        fa_dma16(fa_rsrc(fa_uniform(ts.kc + u), nb), ts.ks + (4 * i + wave) * 1024, dkc);
+        fa_dma16(ts.rk, ts.ks + (4 * i + wave) * 1024, voff[n]);
     } else {
-      const int i = n - 8;
-      const int32_t u = __builtin_amdgcn_readfirstlane(8 * (4 * i + wave) * ldkr2);
-      fa_dma16(fa_rsrc(fa_uniform(ts.kr + u), max(0, ts.nb_r - u)), ts.ks + FA_KR + (4 * i + wave) * 1024, dkr);
+      fa_dma16(ts.rr, ts.ks + FA_KR + (4 * (n - 8) + wave) * 1024, voff[n]);
     }
   };
   auto issue_tile = [&](int t) {

@@ -51,6 +51,27 @@ def test_output_projection_v3_long_rows_sampled():
     assert rel_l2(got[rows], ref) <= BF16_TOL
 
 
+def test_output_projection_ragged_tiles_several_rounds():
+    """More 256 x 256 tiles than one round of workgroups (396) with both a
+    partial last row tile (3000 rows: 184 in the last) and a partial last
+    column tile (8256 columns: 64 in the last).  Rows sampled from every row
+    tile, every column checked."""
+    s = mi.V3
+    T, d, H = 3000, 8256, 32
+    cfg = config(s)
+    cfg.d_model = d
+    cfg.n_heads = H
+    x = _rand(79, (T, H * s.d_head))
+    w_o = _rand(80, (d, H * s.d_head), std=(H * s.d_head) ** -0.5)
+    got = _project(cfg, x, w_o, torch.bfloat16)
+    rows = np.array([0, 1, 255, 256, 700, 1500, 2047, 2815, 2816, 2999])
+    ref = om.output_projection(x[rows].reshape(len(rows), H, s.d_head), w_o)
+    err = rel_l2(got[rows], ref)
+    print(f"rel_l2={err:.3e}")
+    assert err <= BF16_TOL
+    assert np.isfinite(got).all()
+
+
 def test_folded_output_projection():
     """W^O' applied to the latent sums equals W^O applied to the heads'
     outputs (d_model reduced to 1024 to keep the float64 oracle quick)."""
