@@ -785,32 +785,34 @@ __global__ __launch_bounds__(256) void merge_wuv_bf16_kernel(AttnArgs a, const b
   const int32_t* row_off = a.plan + 2;
   int i0[NR], n[NR];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int r = r0 + wave + 4 * i;
-    i0[i] = r < n_rows ? row_off[r] : 0;
-    n[i] = r < n_rows ? row_off[r + 1] - i0[i] : 0;
+  for (int i = 0; i < NR; ++i) {  // (unguarded: a row past the batch reads the last row's offsets)
+    const int r = r0 + wave + 4 * i, rc = min(r, max(n_rows - 1, 0));
+    const int b0 = row_off[rc], b1 = row_off[rc + 1];
+    i0[i] = r < n_rows ? b0 : 0;
+    n[i] = r < n_rows ? b1 - b0 : 0;
   }
   u32x4 v[NR][MW_BATCH];
   float mk[NR][MW_BATCH], lk[NR][MW_BATCH];
+  // The loads are unguarded (a slot past a row's last reads the last one, a
+  // row with one chunk reads its o_lat row, a row past the batch the last
+  // row's) and the unused values are dropped by selects: guarded loads each
+  // waited for the one before.
+  const int last_row = max(n_rows - 1, 0);
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     const int r = r0 + wave + 4 * i;
+    const bool one = n[i] == 1;  // one chunk: the attention kernel wrote o_lat itself
+    const int last = max(n[i] - 1, 0);
+    const bf16* orow = (const bf16*)a.o_lat + ((int64_t)min(r, last_row) * H + head) * DC + 8 * lane;
 #pragma unroll
     for (int k = 0; k < MW_BATCH; ++k) {
-      mk[i][k] = -INFINITY;
-      lk[i][k] = 0.f;
-      v[i][k] = u32x4{0u, 0u, 0u, 0u};
-      if (n[i] == 1 && k == 0) {  // one chunk: the attention kernel wrote o_lat itself
-        mk[i][0] = 0.f;
-        lk[i][0] = 1.f;
-        v[i][0] = ld16((const bf16*)a.o_lat + ((int64_t)r * H + head) * DC + 8 * lane);
-      } else if (n[i] > 1 && k < n[i]) {
-        const int64_t slot = (int64_t)(i0[i] + k) * H + head;
-        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
-        mk[i][k] = ml.x;
-        lk[i][k] = ml.y;
-        v[i][k] = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
-      }
+      const int64_t slot = (int64_t)(i0[i] + min(k, last)) * H + head;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+      const u32x4 x = ld16(one ? orow : (const bf16*)a.part_o + slot * DC + 8 * lane);
+      const bool valid = one ? k == 0 : k < n[i];
+      v[i][k] = valid ? x : u32x4{0u, 0u, 0u, 0u};
+      mk[i][k] = valid ? (one ? 0.f : ml.x) : -INFINITY;
+      lk[i][k] = valid ? (one ? 1.f : ml.y) : 0.f;
     }
   }
 #pragma unroll
@@ -821,8 +823,7 @@ __global__ __launch_bounds__(256) void merge_wuv_bf16_kernel(AttnArgs a, const b
       float mb = mstar;
 #pragma unroll
       for (int k = 0; k < MW_BATCH; ++k) mb = fmaxf(mb, mb_[k]);
-      if (mb == -INFINITY) return;
-      const float alpha = exp2f(mstar - mb);
+      const float alpha = mb == -INFINITY ? 1.f : exp2f(mstar - mb);  // (no branch on loaded values)
       L *= alpha;
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc[d] *= alpha;
@@ -844,16 +845,13 @@ __global__ __launch_bounds__(256) void merge_wuv_bf16_kernel(AttnArgs a, const b
       float mb_[MW_BATCH], lb[MW_BATCH];
 #pragma unroll
       for (int k = 0; k < MW_BATCH; ++k) {
-        mb_[k] = -INFINITY;
-        lb[k] = 0.f;
-        vb[k] = u32x4{0u, 0u, 0u, 0u};
-        if (k0 + k < n[i]) {
-          const int64_t slot = (int64_t)(i0[i] + k0 + k) * H + head;
-          const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
-          mb_[k] = ml.x;
-          lb[k] = ml.y;
-          vb[k] = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
-        }
+        const int64_t slot = (int64_t)(i0[i] + min(k0 + k, n[i] - 1)) * H + head;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+        const u32x4 x = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
+        const bool valid = k0 + k < n[i];
+        mb_[k] = valid ? ml.x : -INFINITY;
+        lb[k] = valid ? ml.y : 0.f;
+        vb[k] = valid ? x : u32x4{0u, 0u, 0u, 0u};
       }
       add_batch(vb, mb_, lb);
     }
@@ -880,6 +878,126 @@ __global__ __launch_bounds__(256) void merge_wuv_bf16_kernel(AttnArgs a, const b
     const int r = r0 + 8 * (i >> 2) + 4 * hi + (i & 3);
     if (r < n_rows) out[((int64_t)r * H + head) * 128 + 32 * wave + l32] = (bf16)acc[i];
   }
+}
+
+// The same merge and W^UV for a few query rows with many splits each (long
+// contexts): one workgroup per (row, head), so the grid has rows x H
+// workgroups instead of H, and the row's partials are shared out over the
+// four waves (wave w takes splits w, w + 4, ...), each keeping four loads in
+// flight; the waves' (m*, L, acc) are combined through LDS.  o_lat goes to
+// row 0 of the 32-row MFMA operand and only output row 0 is stored.
+// Workgroup ids run head-fastest, so the workgroups of one head (sharing
+// W_i^UV) are on one XCD.
+constexpr int MR_BATCH = 4;  // partials per wave loaded together
+__global__ __launch_bounds__(256) void merge_wuv_row_bf16_kernel(AttnArgs a, const bf16* __restrict__ w_uv,
+                                                                 bf16* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char ot[MW_ROWS * MW_RS];
+  __shared__ float cm[4], cl[4];
+  __shared__ __attribute__((aligned(16))) float cacc[4][DC];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int H = a.H, head = (int)(blockIdx.x % H), r = (int)(blockIdx.x / H);
+  // B operand of step s: W^UV row head*128 + 32 wave + l32, columns 16 s + 8 hi .. + 7
+  const bf16* wrow = w_uv + ((int64_t)head * 128 + 32 * wave + l32) * DC + 8 * hi;
+  u32x4 bw[DC / 16];
+#pragma unroll
+  for (int s = 0; s < DC / 16; ++s) bw[s] = ld16(wrow + 16 * s);
+
+  const int32_t* row_off = a.plan + 2;
+  const int i0 = row_off[r], n = row_off[r + 1] - i0;
+  float mstar = -INFINITY, L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (n == 1) {  // one chunk: the attention kernel wrote o_lat itself
+    if (wave == 0) {
+      const u32x4 x = ld16((const bf16*)a.o_lat + ((int64_t)r * H + head) * DC + 8 * lane);
+      mstar = 0.f;
+      L = 1.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] = bf16_lo(x[d]);
+        acc[2 * d + 1] = bf16_hi(x[d]);
+      }
+    }
+  } else {
+    for (int k0 = wave; k0 < n; k0 += 4 * MR_BATCH) {
+      u32x4 vb[MR_BATCH];
+      float mb_[MR_BATCH], lb[MR_BATCH];
+      // unguarded loads (a split past the row's last reads the last one and
+      // is dropped by the selects), so all of a batch's loads are in flight
+      // together: guarded ones each waited for the one before
+#pragma unroll
+      for (int k = 0; k < MR_BATCH; ++k) {
+        const int kk = k0 + 4 * k;
+        const int64_t slot = (int64_t)(i0 + min(kk, n - 1)) * H + head;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot * 2);
+        const u32x4 x = ld16((const bf16*)a.part_o + slot * DC + 8 * lane);
+        const bool valid = kk < n;
+        mb_[k] = valid ? ml.x : -INFINITY;
+        lb[k] = valid ? ml.y : 0.f;
+        vb[k] = valid ? x : u32x4{0u, 0u, 0u, 0u};
+      }
+      float mb = mstar;
+#pragma unroll
+      for (int k = 0; k < MR_BATCH; ++k) mb = fmaxf(mb, mb_[k]);
+      // (no branch on the loaded values: it would hold up the batch's loads)
+      const float alpha = mb == -INFINITY ? 1.f : exp2f(mstar - mb);
+      L *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+      mstar = mb;
+#pragma unroll
+      for (int k = 0; k < MR_BATCH; ++k) {
+        const float wk = lb[k] > 0.f ? exp2f(mb_[k] - mstar) * lb[k] : 0.f;
+        L += wk;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] += wk * bf16_lo(vb[k][d]);
+          acc[2 * d + 1] += wk * bf16_hi(vb[k][d]);
+        }
+      }
+    }
+  }
+  // combine the four waves: o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) L_w
+  if (lane == 0) {
+    cm[wave] = mstar;
+    cl[wave] = L;
+  }
+  *reinterpret_cast<f32x4*>(&cacc[wave][8 * lane]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(&cacc[wave][8 * lane + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  __syncthreads();
+  if (wave == 0) {
+    const float M = fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3]));
+    float Lt = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = cl[w] > 0.f ? exp2f(cm[w] - M) : 0.f;
+      Lt += sc * cl[w];
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&cacc[w][8 * lane]);
+      const f32x4 hv = *reinterpret_cast<const f32x4*>(&cacc[w][8 * lane + 4]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        o[d] += sc * lo[d];
+        o[4 + d] += sc * hv[d];
+      }
+    }
+    u32x4 res = {0u, 0u, 0u, 0u};
+    if (Lt > 0.f) {
+      const float inv = 1.f / Lt;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) res[d] = pack_bf16x2(o[2 * d] * inv, o[2 * d + 1] * inv);
+    }
+    *reinterpret_cast<u32x4*>(ot + 16 * lane) = res;  // row 0 of the A operand
+  }
+  __syncthreads();
+  // out[r, head, n] = sum_k o_lat[r, k] W^UV[head*128 + n, k]: rows 1..31 of the
+  // operand are not read into any stored value (each output row depends on its
+  // own operand row only)
+  f32x16 accm;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) accm[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DC / 16; ++s)
+    accm = mfma32(*reinterpret_cast<const u32x4*>(ot + l32 * MW_RS + (2 * s + hi) * 16), bw[s], accm);
+  // lane (l32, hi = 0), register 0: row 0, column 32 wave + l32
+  if (hi == 0) out[((int64_t)r * H + head) * 128 + 32 * wave + l32] = (bf16)accm[0];
 }
 
 // Work plan: one workgroup of 256 threads (wave-level scans, three barriers
@@ -992,8 +1110,14 @@ hipError_t launch_merge_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_merge_wuv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t st) {
-  const int64_t n = (int64_t)a.H * ((a.B * a.s_q + MW_ROWS - 1) / MW_ROWS);
-  if (n <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)a.B * a.s_q;
+  if (rows <= 0) return hipSuccess;
+  if (rows <= MW_ROWS) {  // a few rows: one workgroup per (row, head)
+    hipLaunchKernelGGL(merge_wuv_row_bf16_kernel, dim3((unsigned)(rows * a.H)), dim3(256), 0, st, a,
+                       (const bf16*)w_uv, (bf16*)out);
+    return hipGetLastError();
+  }
+  const int64_t n = (int64_t)a.H * ((rows + MW_ROWS - 1) / MW_ROWS);
   hipLaunchKernelGGL(merge_wuv_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a, (const bf16*)w_uv, (bf16*)out);
   return hipGetLastError();
 }
