@@ -392,35 +392,45 @@ void fa_bf16_kernel(FaArgs a) {
         for (int qb = 0; qb < 2; ++qb) mh[qb] = need[qb] ? mx[qb] : m_run[qb];  // new running max
       } else if constexpr (j == 22) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) alpha[qb] = m_run[qb] - mh[qb];
-      }
-      if constexpr (j == 23) {
+        for (int qb = 0; qb < 2; ++qb) alpha[qb] = m_run[qb] - mh[qb];  // (exponentiated only when used)
+      } else if constexpr (j == 23) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          alpha[qb] = __builtin_amdgcn_exp2f(alpha[qb]);
-          m_run[qb] = mh[qb];
-        }
+        for (int qb = 0; qb < 2; ++qb) m_run[qb] = mh[qb];
       }
-      // pair k of scores: x = s * scale - m at slot 23 + 2k, exp at 24 + 2k,
-      // bf16 pack into P^T at 25 + 2k
+      // score e (0..63, pair k = e/2, half e%2): x = s * scale - m at slot
+      // 22 + e, its exponential at 23 + e, the pair's bf16 pack into P^T at
+      // 25 + 2k.  One exponential per slot: v_exp_f32 issues at a quarter of
+      // the VALU rate, and two in one slot outlasted the MFMA they shadow.
       if constexpr (j >= 25 && (j - 25) % 2 == 0 && (j - 25) / 2 < 32) {
         constexpr int k = (j - 25) / 2, qb = k >> 4, kb = (k >> 3) & 1, h2 = (k >> 2) & 1, e = k & 3;
         pc[2 * kb + h2][qb][e] = pack_bf16x2(ea, eb);
       }
-      if constexpr (j >= 24 && (j - 24) % 2 == 0 && (j - 24) / 2 < 32) {
-        ea = __builtin_amdgcn_exp2f(xa);
-        eb = __builtin_amdgcn_exp2f(xb);
+      if constexpr (j >= 23 && j - 23 < 64) {
+        if constexpr ((j - 23) % 2 == 0)
+          ea = __builtin_amdgcn_exp2f(xa);
+        else
+          eb = __builtin_amdgcn_exp2f(xb);
       }
-      if constexpr (j >= 23 && (j - 23) % 2 == 0 && (j - 23) / 2 < 32) {
-        constexpr int k = (j - 23) / 2, qb = k >> 4, kb = (k >> 3) & 1, h2 = (k >> 2) & 1, e = k & 3;
-        constexpr int i = 8 * h2 + 2 * e;
-        xa = __builtin_fmaf(sc[kb][qb][i], scale_log2, -mh[qb]);
-        xb = __builtin_fmaf(sc[kb][qb][i + 1], scale_log2, -mh[qb]);
+      if constexpr (j >= 22 && j - 22 < 64) {
+        constexpr int sc_e = j - 22, k = sc_e / 2, qb = k >> 4, kb = (k >> 3) & 1, h2 = (k >> 2) & 1, e = k & 3;
+        constexpr int i = 8 * h2 + 2 * e + (sc_e % 2);
+        if constexpr (sc_e % 2 == 0)
+          xa = __builtin_fmaf(sc[kb][qb][i], scale_log2, -mh[qb]);
+        else
+          xb = __builtin_fmaf(sc[kb][qb][i], scale_log2, -mh[qb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // P^T of tile t is consumed here, in this block: otherwise the compiler
+    // sinks the whole softmax past the rescale branch into the next step's
+    // block, where it runs as one burst between two MFMAs instead of in the
+    // slots above
+    asm volatile("" ::"v"(pc[0][0]), "v"(pc[0][1]), "v"(pc[1][0]), "v"(pc[1][1]), "v"(pc[2][0]), "v"(pc[2][1]),
+                 "v"(pc[3][0]), "v"(pc[3][1]));
     // the accumulator now holds tiles <= t-1 at the old running max
     if (need[0] || need[1]) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) alpha[qb] = __builtin_amdgcn_exp2f(alpha[qb]);
       asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
