@@ -14,7 +14,7 @@
 // Three kernels by shape:
 //  * gemm_big_kernel: at least 256 rows and enough tiles to fill the CUs
 //    (the prefill projections): 256 x 256 / 256 x 192 tiles, see below.
-//  * gemm_smallm_bf16_kernel: at most 64 rows, K <= 512 (decode projections).
+//  * gemm_smallm_bf16_kernel: at most 256 rows, K <= 512 (decode projections).
 //  * gemm_bf16_kernel: everything else, including B given [K, N].  Tiles
 //    128 x 128 x 64, four waves in a 2 x 2 arrangement, each wave a 64 x 64
 //    block of four 32 x 32 MFMA accumulators; A and B tiles staged through
@@ -544,9 +544,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 
 // ---------------------------------------------------------------------------
-// Small-M batched GEMM (decode: M = query rows <= 64 per head, K <= 512): one
-// workgroup per (64-column block, batch entry) holds the whole K extent of
-// its A and B tiles in LDS, so it makes one round of loads instead of a
+// Small-M batched GEMM (decode: M = query rows <= 256 per head, K <= 512): one
+// workgroup per (64-column block, batch entry, 64-row block) holds the whole
+// K extent of its A and B tiles in LDS, so it makes one round of loads instead of a
 // pipeline of K slices, and the many small workgroups keep enough loads in
 // flight.  Four waves in a 2 x 2 arrangement of 32 x 32 MFMA tiles.  The
 // output tile is staged in LDS and written with 16-byte stores.
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g, PlanJ
     // columns past the batch pad the grid width to a multiple of 8 (so each
     // batch entry keeps its XCD); the first of them builds the attention plan
     if ((int)blockIdx.x >= g.batch) {
-      if ((int)blockIdx.x == g.batch && blockIdx.y == 0)
+      if ((int)blockIdx.x == g.batch && blockIdx.y == 0 && blockIdx.z == 0)
         plan_body(pj.a, pj.plan, pj.target_items, pj.min_chunk, pj.max_chunk);
       return;
     }
@@ -570,18 +570,20 @@ __global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g, PlanJ
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  // grid (batch, column blocks): consecutive workgroups (which the dispatcher
-  // deals round-robin to the XCDs) take different batch entries, so the column
-  // blocks of one batch entry share an XCD and its L2 copy of the A tile
-  const int n0 = blockIdx.y * SM_BN, z = blockIdx.x;
+  // grid (batch, column blocks, row blocks of 64): consecutive workgroups
+  // (which the dispatcher deals round-robin to the XCDs) take different batch
+  // entries, so the column and row blocks of one batch entry share an XCD and
+  // its L2 copies of the A and B tiles
+  const int n0 = blockIdx.y * SM_BN, z = blockIdx.x, m0 = blockIdx.z * SM_BM;
+  const int Mb = min(SM_BM, g.M - m0);  // rows of this block
   const int K = g.K, kc = K / 8;  // 16-byte chunks per row
-  const bf16* A = (const bf16*)g.A + z * g.strideA;
+  const bf16* A = (const bf16*)g.A + z * g.strideA + (int64_t)m0 * g.lda;
   const bf16* B = (const bf16*)g.B + z * g.strideB;
 
   // All loads are issued before any LDS store so they are in flight together.
   constexpr int PER = SM_BM * (KMAX / 8) / 256;  // 16-byte chunks per thread and operand
   // A rows past M load as zero
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (int64_t)(g.M - 1) * g.lda * 2 + K * 2);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (int64_t)(Mb - 1) * g.lda * 2 + K * 2);
   u32x4 va[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -648,10 +650,10 @@ __global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g, PlanJ
   for (int i = 0; i < 16; ++i)
     sc[(32 * wm + 8 * (i >> 2) + 4 * hi + (i & 3)) * (CS / 2) + 32 * wn + l32] = (bf16)acc[i];
   __syncthreads();
-  bf16* C = (bf16*)g.C + z * g.strideC;
+  bf16* C = (bf16*)g.C + z * g.strideC + (int64_t)m0 * g.ldc;
   for (int c = tid; c < SM_BM * (SM_BN / 8); c += 256) {
     const int r = c / (SM_BN / 8), c8 = c % (SM_BN / 8);
-    if (r < g.M && n0 + 8 * c8 < g.N)
+    if (r < Mb && n0 + 8 * c8 < g.N)
       *(u32x4*)(C + (int64_t)r * g.ldc + n0 + 8 * c8) = *(const u32x4*)(sa + r * CS + c8 * 16);
   }
 }
@@ -659,14 +661,15 @@ __global__ __launch_bounds__(256) void gemm_smallm_bf16_kernel(GemmArgs g, PlanJ
 }  // namespace
 
 namespace {
+constexpr int SM_MAX_ROWS = 4 * SM_BM;  // up to 4 row blocks
 bool smallm_form(const GemmArgs& g) {
-  return g.M <= SM_BM && g.K <= 512 && g.K % 64 == 0 && g.N % 8 == 0 && g.out_bf16 && !g.B2;
+  return g.M <= SM_MAX_ROWS && g.K <= 512 && g.K % 64 == 0 && g.N % 8 == 0 && g.out_bf16 && !g.B2;
 }
 
 template <bool PLAN>
 void launch_smallm(const GemmArgs& g, const PlanJob& pj, hipStream_t st) {
   const unsigned gx = PLAN ? (unsigned)((g.batch + 1 + 7) / 8 * 8) : (unsigned)g.batch;
-  dim3 grid(gx, (unsigned)((g.N + SM_BN - 1) / SM_BN));
+  dim3 grid(gx, (unsigned)((g.N + SM_BN - 1) / SM_BN), (unsigned)((g.M + SM_BM - 1) / SM_BM));
   if (g.K <= 128) {
     if (g.b_kn)
       hipLaunchKernelGGL((gemm_smallm_bf16_kernel<true, 128, PLAN>), grid, dim3(256), 0, st, g, pj);
