@@ -397,9 +397,15 @@ def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope,
         _check(lib().mla_decode_profiled(*args, *attn_events), where)
 
 
-def mla_stream_read(src, stream=None) -> None:
-    """Read all of src (a contiguous GPU tensor) once: the HBM read ceiling."""
+def mla_stream_read(src, sink=None, stream=None) -> None:
+    """Read all of src (a contiguous GPU tensor) once: the HBM read ceiling.
+    sink (optional, a GPU int32 tensor) receives 0x9E3779B9 only when that is
+    the XOR of all 32-bit words read, which lets a test check that every word
+    is read exactly once."""
     where = "mla_stream_read"
     _tensor(where, "src", src)
-    _on_gpu(where, src=src)
-    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(), None, _stream(stream)), where)
+    if sink is not None:
+        _tensor(where, "sink", sink, torch.int32)
+    _on_gpu(where, src=src, sink=sink)
+    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                 None if sink is None else _ptr(sink), _stream(stream)), where)

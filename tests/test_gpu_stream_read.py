@@ -1,0 +1,57 @@
+"""The streaming-read helper that times the HBM read ceiling reads every
+16-byte word of its buffer.
+
+Each thread of the kernel XORs the words it reads and writes the sink only
+when the XOR of its four 32-bit lanes equals 0x9E3779B9.  With a zero buffer
+the sink is never written; with that value planted in one word, the sink is
+written exactly when some thread read that word (an odd number of times).
+Planted words sit at the ends of tiles, the middle and the ragged tail, for
+one word, a part tile, one tile, one tile per workgroup and several tiles per
+workgroup plus a tail.
+"""
+import pytest
+import torch
+
+import head_latent_attention_06_amd as mla
+
+pytestmark = pytest.mark.gpu
+
+MAGIC = 0x9E3779B9 - (1 << 32)  # as a signed int32
+TILE16 = 256 * 9  # 16-byte words per tile
+
+
+def _cus() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _sizes():
+    g = _cus()
+    return [1, 255, TILE16, TILE16 * g, TILE16 * g * 5 + 1000]
+
+
+@pytest.mark.parametrize("si", range(5))
+def test_every_word_read(si):
+    n16 = _sizes()[si]
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    ntiles = n16 // TILE16
+    words = {0, n16 - 1, n16 // 2, TILE16 - 1, TILE16, ntiles * TILE16, ntiles * TILE16 - 1, n16 - 2}
+    for w in sorted(x for x in words if 0 <= x < n16):
+        for lane in (0, 3):
+            buf[4 * w + lane] = MAGIC
+            sink.zero_()
+            mla.mla_stream_read(buf, sink)
+            torch.cuda.synchronize()
+            assert int(sink.item()) == MAGIC, (n16, w, lane)
+            buf[4 * w + lane] = 0
+
+
+def test_rejects_ragged_and_misaligned():
+    b = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mla.MLAError):
+        mla.mla_stream_read(b[:17])
+    with pytest.raises(mla.MLAError):
+        mla.mla_stream_read(b[1:33])
