@@ -22,6 +22,7 @@
 // domain with the lazy rescale of the latent kernel.
 #include <math.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "mla_device.h"
@@ -150,23 +151,35 @@ __device__ __forceinline__ void fa_scale_tuple(f32x16& t, float alpha) {
 #undef FA_SCALE1
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fa_bf16_kernel(FaArgs a) {
+// One work item: 256 queries of one head of one sequence, its key tiles
+// taken in ascending order, or in descending order when desc is set (the
+// online softmax does not depend on the order; the schedule below uses it to
+// keep workgroups on the same keys).  The caller separates consecutive items
+// by a barrier.
+__device__ __forceinline__ void fa_item(const FaArgs& a, const int work, const bool desc) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[FA_LDS];
-  const int tid = threadIdx.x;
+  // opaque, so the per-lane values below are computed per item rather than
+  // hoisted out of the caller's item loop (where they would stay live)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   // work id -> (sequence, head, query group): the query groups of one head are
-  // consecutive ids, run longest first, and consecutive ids share an XCD (and
-  // its L2), so a head's k^C / v^C stream is read from HBM about once
+  // consecutive ids, longest first
   const int H = a.H;
   const int n_qg = (a.L + FA_QG - 1) / FA_QG;
-  const int work = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int q0 = (n_qg - 1 - work % n_qg) * FA_QG;
   const int head = (work / n_qg) % H, b = work / n_qg / H;
   // keys [0, start_pos + last query of the workgroup]
   const int kv_hi = a.start_pos + min(q0 + FA_QG, a.L);
   const int ntiles = (kv_hi + FA_KT - 1) / FA_KT;
+  // Tile steps run in pairs (the two score and P^T buffers swap roles): the
+  // workgroup passes nt_all steps, ntiles rounded up to even.  Step t takes
+  // key tile t, or nt_all - 1 - t in descending order; a tile past kv_hi
+  // (the rounding, and steps past nt_all whose loads are issued by the
+  // pipeline) loads as zeros and is masked by causality.
+  const int nt_all = (ntiles + 1) & ~1;
+  auto key_tile = [&](int t) { return desc ? nt_all - 1 - t : t; };
   const float scale_log2 = a.scale * FA_LOG2E;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
@@ -197,8 +210,9 @@ void fa_bf16_kernel(FaArgs a) {
     uint32_t ks, vs;
   };
   auto tile_src = [&](int t) {
-    const int kb0 = t * FA_KT;
-    const int rows = max(0, min(FA_KT, kv_hi - kb0));
+    const int kt = key_tile(t);
+    const int kb0 = max(kt, 0) * FA_KT;
+    const int rows = kt < 0 ? 0 : max(0, min(FA_KT, kv_hi - kb0));
     TileSrc ts;
     const int32_t nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
     const int32_t nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
@@ -278,10 +292,15 @@ void fa_bf16_kernel(FaArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc_l[qb][i] = 0.f;
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
-  float m_run[2] = {-INFINITY, -INFINITY};
+  // running max floor: finite, so a row whose first tiles are all masked (in
+  // descending order) gets p = 2^(-inf) = 0 there, not inf - inf
+  float m_run[2] = {-1e30f, -1e30f};
   const int qpos0 = a.start_pos + q0 + FA_QW * wave;  // position of the wave's first query
   // tiles whose keys are all after every query of this wave are only moved, not used
-  const int nt_wave = min(ntiles, (qpos0 + FA_QW - 1) / FA_KT + 1);
+  // Ascending: tiles whose keys are all after every query of this wave are only
+  // moved, not used.  Descending: such tiles come first, and the wave runs
+  // them masked (its SIMD would wait at the barriers anyway).
+  const int nt_wave = desc ? nt_all : min(ntiles, (qpos0 + FA_QW - 1) / FA_KT + 1);
 
   f32x16 sA[2][2], sB[2][2];  // S^T [key block][query block] of two consecutive tiles
   u32x4 pA[4][2], pB[4][2];   // P^T [key step][query block] of two consecutive tiles
@@ -299,14 +318,15 @@ void fa_bf16_kernel(FaArgs a) {
     const uint32_t kq = smem_addr + ((t + 1) % FA_NK) * FA_KSTAGE + kx;
     const uint32_t rq = smem_addr + ((t + 1) % FA_NK) * FA_KSTAGE + rx;
     const uint32_t vq = smem_addr + FA_VBASE + ((t + FA_NV - 1) % FA_NV) * FA_VSTAGE + vx;
-    if (t * FA_KT + FA_KT - 1 > qpos0) {
-      // a tile on the diagonal: key t*64 + 32 kb + 8 (i/4) + 4 hi + i%4 is
-      // masked for query qpos0 + 32 qb + l32 when 8 (i/4) + i%4 exceeds thr
+    const int kt = key_tile(t);
+    if (kt * FA_KT + FA_KT - 1 > qpos0) {
+      // a tile on (or past) the diagonal: key kt*64 + 32 kb + 8 (i/4) + 4 hi + i%4
+      // is masked for query qpos0 + 32 qb + l32 when 8 (i/4) + i%4 exceeds thr
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          fa_causal_mask(sc[kb][qb], qpos0 + 32 * qb + l32 - t * FA_KT - 32 * kb - 4 * hi);
+          fa_causal_mask(sc[kb][qb], qpos0 + 32 * qb + l32 - kt * FA_KT - 32 * kb - 4 * hi);
     }
     // MFMA order: 44 units of two MFMAs (query blocks 0, 1), interleaving
     // S^T of tile t+1 with O^T += V^T P^T of tile t-1 so the transposing
@@ -380,8 +400,8 @@ void fa_bf16_kernel(FaArgs a) {
         }
       } else if constexpr (j == 19) {
         // running max, raised only when the tile max exceeds it by more than
-        // FA_SLACK (p <= 2^8 stays exact in fp32); a query's first tile always
-        // holds key 0, so there the tile max is finite and alpha = 0
+        // FA_SLACK (p <= 2^8 stays exact in fp32); from the floor, the first
+        // tile with a visible key raises it, with alpha = 2^(-1e30 - m) = 0
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) need[qb] = __any(mx[qb] > mh[qb]);
       } else if constexpr (j == 20) {
@@ -495,11 +515,10 @@ void fa_bf16_kernel(FaArgs a) {
   // wait states before VALU reads the MFMA results
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // Tile steps run in pairs (the two score and P^T buffers swap roles), so a
-  // wave with an odd tile count runs one more, all of whose keys are after its
-  // queries: fully masked, it adds nothing.  Every wave passes the same number
-  // of barriers, one per tile step up to ntiles rounded up to even.
-  const int nt_even = (nt_wave + 1) & ~1, nt_all = (ntiles + 1) & ~1;
+  // A wave with an odd tile count runs one more, all of whose keys are after
+  // its queries: fully masked, it adds nothing.  Every wave passes the same
+  // number of barriers, one per tile step up to nt_all.
+  const int nt_even = (nt_wave + 1) & ~1;
   int t = 0;
   for (; t < nt_even; t += 2) {
     sync();
@@ -550,6 +569,39 @@ void fa_bf16_kernel(FaArgs a) {
   }
 }
 
+// Persistent workgroups, one per CU (the LDS allows no second): workgroup g
+// runs on XCD g % 8 and takes items of that XCD's contiguous range of work
+// ids (head after head, each head's query groups longest first).  The P
+// workgroups of an XCD take the range in rounds of P ids, in snake order
+// (slot k takes id k of an even round and id P-1-k of an odd one): with P
+// query groups per head, each pair of rounds gives every workgroup one long
+// and one short item of equal total length, so the workgroups stay in step.
+// Even rounds run their key tiles upward and odd rounds downward: all items
+// of an even round start together and are at the same key tile at any
+// moment; an odd-round item starts when its slot's even-round item ends,
+// and counting down from its own top tile it, too, is at the same tile as
+// every other odd-round item.  So the XCD's L2 holds the few tiles of at
+// most two heads that all its workgroups are reading.  (One workgroup per
+// item left each CU idle for a median 11.5 us between items, as the
+// dispatcher did not hand the next workgroup to the CU just freed; and
+// persistent rounds that all ran upward, the odd ones starting staggered,
+// fetched 2.6 times the bytes from HBM.)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bf16_kernel(FaArgs a, int n_work) {
+  const int G = (int)gridDim.x, g = (int)blockIdx.x, x = g % 8, k = g / 8;
+  const int q = n_work / 8, r = n_work % 8;
+  const int n_x = q + (x < r ? 1 : 0), base = x * q + min(x, r);  // this XCD's ids
+  const int P = (G - x + 7) / 8;                                    // its workgroups
+  bool first = true;
+  for (int rd = 0; rd * P < n_x; ++rd) {
+    const int i = rd * P + ((rd & 1) ? P - 1 - k : k);
+    if (i >= n_x) continue;
+    if (!first) __syncthreads();  // every wave is done with the previous item's LDS
+    first = false;
+    fa_item(a, base + i, (rd & 1) != 0);
+  }
+}
+
 // Rows [0, kv_end) of every sequence from the paged cache into a contiguous
 // [B * kv_end, row] buffer (one 16-byte chunk per thread); a block-table entry
 // outside the pool gives zeros and sets err_flags.
@@ -595,7 +647,12 @@ hipError_t launch_fa_bf16(const FaArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.L <= 0 || a.H <= 0) return hipSuccess;
   const int64_t n = (int64_t)a.H * ((a.L + FA_QG - 1) / FA_QG) * a.B;
   if (n > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fa_bf16_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t grid = std::min<int64_t>(n, std::max(cus, 8));  // one workgroup per CU
+  hipLaunchKernelGGL(fa_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, (int)n);
   return hipGetLastError();
 }
 
