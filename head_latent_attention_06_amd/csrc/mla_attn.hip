@@ -295,8 +295,10 @@ void attn_bf16_kernel(AttnArgs a) {
   auto scale_of = [&](const TileDma& d) { return buf_ld4f(d.r, cv_r * F_RB + F_SCALE + 4 * wave); };
   float scl_cv = 0.f, scl_nx = 0.f;  // scales of the tile decoded next, and of the one after
 
-  // ---- tiles 0 .. DEPTH-1 (possibly empty), then the queries: one burst
-  // (FP8: tiles 0 and 1 are decoded once they land, tile 2 stays in flight)
+  // ---- tiles 0 .. DEPTH-2 (possibly empty), then the queries: one burst
+  // (bf16: tile DEPTH-1 goes out after the first tile's scores, so the
+  // queries, which those scores need whole, are not queued behind it; FP8:
+  // tiles 0 and 1 are decoded once they land, tile 2 stays in flight)
   TileDma d0 = issue_next(split_pages[0]);
   if constexpr (FP8) {
     scl_cv = scale_of(d0);
@@ -304,7 +306,7 @@ void attn_bf16_kernel(AttnArgs a) {
     scl_nx = scale_of(d0);
   } else {
 #pragma unroll
-    for (int p = 1; p < DEPTH; ++p) issue_next(cursor_page());
+    for (int p = 1; p < DEPTH - 1; ++p) issue_next(cursor_page());
   }
   // Q^T fragments: B operand of S^T = K Q^T; k step j covers dims 16j .. 16j+15
   // (j < 32: q_lat, j >= 32: q^R).  Heads past H load as zero.
@@ -362,8 +364,8 @@ void attn_bf16_kernel(AttnArgs a) {
     scl_cv = scale_of(issue_next(cursor_page()));
   }
   // page of the next tile to issue, fetched one tile early to keep the LDS
-  // latency off the issue path
-  int next_page = cursor_page();
+  // latency off the issue path (bf16: once the prologue's last tile is out)
+  int next_page = FP8 ? cursor_page() : 0;
 
   // Accumulator O^T for this wave's 128 latent dims (4 blocks of 32) and all
   // 128 heads of the workgroup (4 blocks of 32): acc[4 * d + hb].
@@ -504,9 +506,9 @@ void attn_bf16_kernel(AttnArgs a) {
     flag_xchg[wave] = resc ? 1 : 0;             // every lane stores the same byte
   };
   f32x16 s_nx;  // scores of the next tile
-  // bf16: tile 0 has landed once at most tiles 1 .. DEPTH-1 and the 36 query
+  // bf16: tile 0 has landed once at most tiles 1 .. DEPTH-2 and the 36 query
   // loads are outstanding (loads complete in order); FP8: everything has
-  if constexpr (!FP8) wait_vmcnt<(DEPTH - 1) * DMA_PER_THREAD + 36>();
+  if constexpr (!FP8) wait_vmcnt<(DEPTH - 2) * DMA_PER_THREAD + 36>();
   __syncthreads();
   {
     const unsigned char* K0 = smem;
@@ -515,6 +517,13 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int j = 0; j < 36; ++j) {
       qk_step(K0, j, s_nx);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // bf16: tile DEPTH-1, after the last wait for a query fragment (the
+    // compiler's waits for them do not count loads issued in asm, so a tile
+    // issued earlier would be waited for with them)
+    if constexpr (!FP8) {
+      issue_next(cursor_page());
+      next_page = cursor_page();
     }
 #pragma unroll
     for (int j = 0; j < SM_SLOTS; ++j) sm_slot(j, s_nx, k0, true);
