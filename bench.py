@@ -439,7 +439,8 @@ def attention_sources_sha256() -> str:
 def run_ceilings(steps: int = 20) -> dict:
     """Measured ceilings on this GPU: a plain streaming read of 4 GiB (the
     library's own read kernel), the library's large-tile bf16 GEMM at
-    8192 x 8192 x 8192 (through the output-projection entry point), and the
+    8192 x 8192 x 8192 (through the output-projection entry point), a stream
+    of independent MFMAs on random operands (both instruction shapes), and the
     vendor GEMM library on the same product."""
     res = {}
     src = torch.ones(1 << 31, dtype=torch.int16, device="cuda")  # 4 GiB
@@ -480,6 +481,28 @@ def run_ceilings(steps: int = 20) -> dict:
                         "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                         "frac_of_spec": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del u, ws
+    # The matrix cores alone: independent MFMAs on random bf16 operands (the
+    # library's mfma_rate_kernel), both instruction shapes.
+    ops = torch.randn(1 << 20, device="cuda", generator=g).bfloat16()
+    mf = {"kernel": "mfma_rate_kernel", "operands": "N(0,1) bf16"}
+    for shape in (16, 32):
+        iters = 2000
+        settle(lambda i: mla.mla_mfma_rate(ops, iters, shape), 100.0)
+        ev = HipEvents(steps)
+        hip_stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(steps):
+            ev.hip.hipEventRecord(ev.ev[2 * i], hip_stream)
+            mla.mla_mfma_rate(ops, iters, shape)
+            ev.hip.hipEventRecord(ev.ev[2 * i + 1], hip_stream)
+        torch.cuda.synchronize()
+        ms_m = float(np.median([ev.elapsed_ms(i) for i in range(steps)]))
+        ev.close()
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        tf = cus * 4 * iters * 2 ** 20 / (ms_m * 1e-3) / 1e12
+        mf[f"tflops_{shape}x{shape}"] = round(tf, 1)
+        mf[f"frac_of_spec_{shape}x{shape}"] = round(tf / BF16_PEAK_TFLOPS, 4)
+    res["mfma_bf16"] = mf
+    del ops
     # The vendor GEMM library (torch.mm) on the same operands and layout
     # (x times the transpose of w [N, K]), timed the same way (back-to-back
     # launches after the settle phase, an event pair around each): a second
@@ -507,8 +530,10 @@ def _vs_measured(roof: dict, ceil: dict) -> None:
     if roof.get("unit") == "GB/s" and "hbm_read" in ceil:
         roof["frac_of_measured"] = round(roof["achieved"] / ceil["hbm_read"]["gbs"], 4)
     elif roof.get("unit") == "TFLOP/s" and "gemm_bf16" in ceil:
-        # against the faster of the two measured GEMMs
-        best = max(ceil["gemm_bf16"]["tflops"], ceil.get("gemm_bf16_vendor", {}).get("tflops", 0.0))
+        # against the highest measured matrix-core rate: the MFMA stream, or a
+        # GEMM if one ever ran faster
+        best = max(ceil["gemm_bf16"]["tflops"], ceil.get("gemm_bf16_vendor", {}).get("tflops", 0.0),
+                   ceil.get("mfma_bf16", {}).get("tflops_16x16", 0.0), ceil.get("mfma_bf16", {}).get("tflops_32x32", 0.0))
         roof["frac_of_measured"] = round(roof["achieved"] / best, 4)
 
 

@@ -1,6 +1,7 @@
-// Measurement helper: a plain streaming read of device memory, the HBM
-// ceiling that the decode attention kernel's bandwidth is compared with.
-// Not part of the attention arithmetic.
+// Measurement helpers, not part of the attention arithmetic: a plain
+// streaming read of device memory (the HBM ceiling the decode attention
+// kernel's bandwidth is compared with) and a stream of independent MFMAs (the
+// matrix-core rate the MFMA-bound kernels are compared with).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,6 +55,58 @@ __global__ __launch_bounds__(SR_THREADS) void stream_read_kernel(const u32x4* __
   if (x == 0x9E3779B9u && sink) sink[0] = x;
 }
 
+constexpr int MR_FRAGS = 16;  // 16-byte operand fragments per lane (A and B)
+
+// 2^20 FLOP per wave per round: 64 x (16 x 16 x 32) or 32 x (32 x 32 x 16)
+// (two passes over 16 accumulators), no MFMA depending on the one before.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(const u32x4* __restrict__ ops, int64_t n16, int iters,
+                                                        float* __restrict__ sink) {
+  const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * MR_FRAGS;
+  u32x4 f[MR_FRAGS];
+#pragma unroll
+  for (int k = 0; k < MR_FRAGS; ++k) f[k] = ops[(base + k) % n16];
+  float total = 0.f;
+  if constexpr (SHAPE == 16) {
+    f32x4 acc[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[8 * i + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                   __builtin_bit_cast(bf16x8, f[8 + j]),
+                                                                   acc[8 * i + j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) total += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  } else {
+    f32x16 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)  // two passes over the 16 accumulators, other operands
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[4 * i + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[4 * h + i]),
+                                                                     __builtin_bit_cast(bf16x8, f[8 + 4 * h + j]),
+                                                                     acc[4 * i + j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) total += acc[i][e];
+  }
+  if (total == 1234567.0f && sink) sink[0] = total;
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -67,5 +120,23 @@ extern "C" mla_status mla_stream_read(const void* src, int64_t bytes, void* sink
   const int64_t blocks = cus;  // one workgroup of four waves per CU
   hipLaunchKernelGGL(mla::stream_read_kernel, dim3((unsigned)blocks), dim3(mla::SR_THREADS), 0, (hipStream_t)stream,
                      (const mla::u32x4*)src, n16, (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" mla_status mla_mfma_rate(const void* operands, int64_t bytes, int32_t iters, int32_t shape, void* sink,
+                                   void* stream) {
+  if (!operands || bytes < 262144 || ((uintptr_t)operands & 15) || iters <= 0 || (shape != 16 && shape != 32))
+    return MLA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MLA_ERR_HIP;
+  const int64_t n16 = bytes / 16;
+  if (shape == 16)
+    hipLaunchKernelGGL(mla::mfma_rate_kernel<16>, dim3((unsigned)cus), dim3(256), 0, (hipStream_t)stream,
+                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink);
+  else
+    hipLaunchKernelGGL(mla::mfma_rate_kernel<32>, dim3((unsigned)cus), dim3(256), 0, (hipStream_t)stream,
+                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -282,6 +282,21 @@ mla_status mla_decode_noalloc(const mla_config* cfg, const mla_kv_cache* cache, 
  * impossible case that the XOR of all words read equals 0x9E3779B9. */
 mla_status mla_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 
+/* Measurement helper (not part of the attention arithmetic): the sustained
+ * bf16 matrix-core rate on this device.  One workgroup of four waves per CU;
+ * each wave loads its operand fragments once from `operands` (bf16 values,
+ * e.g. random: the rate depends on the operands' switching activity), then
+ * issues `iters` rounds of independent MFMAs into 256 fp32 accumulators:
+ * shape 16 = v_mfma_f32_16x16x32_bf16 (64 per round), shape 32 =
+ * v_mfma_f32_32x32x16_bf16 (32 per round); 2^20 FLOP per wave per round for
+ * both.  operands 16-byte aligned with bytes >= 262144 (fragments past the
+ * end wrap around), iters > 0, shape 16 or 32, else MLA_ERR_INVALID_ARG.
+ * `sink` (may be NULL, else one writable float) is written only in the
+ * practically impossible case that the accumulators' sum is exactly
+ * 1234567.0. */
+mla_status mla_mfma_rate(const void* operands, int64_t bytes, int32_t iters, int32_t shape, void* sink,
+                         void* stream);
+
 /* Upper bound on the attention work items (split partial slots) mla_decode
  * plans for these sizes; the device plan cuts each query row's visible keys
  * into chunks from the actual kv_lens.  Host helper for tests and sizing;

@@ -1,5 +1,6 @@
-"""The streaming-read helper that times the HBM read ceiling reads every
-16-byte word of its buffer.
+"""The measurement helpers: the streaming read that times the HBM read
+ceiling reads every 16-byte word of its buffer, and the MFMA-rate stream runs
+and validates its arguments.
 
 Each thread of the kernel XORs the words it reads and writes the sink only
 when the XOR of its four 32-bit lanes equals 0x9E3779B9.  With a zero buffer
@@ -55,3 +56,18 @@ def test_rejects_ragged_and_misaligned():
         mla.mla_stream_read(b[:17])
     with pytest.raises(mla.MLAError):
         mla.mla_stream_read(b[1:33])
+
+
+def test_mfma_rate_runs_and_rejects_bad_arguments():
+    ops = torch.randn(1 << 17, device="cuda").bfloat16()  # 256 KiB
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for shape in (16, 32):
+        mla.mla_mfma_rate(ops, 4, shape, sink)
+    torch.cuda.synchronize()
+    assert float(sink.item()) == 0.0  # the accumulators' sum is not the magic value
+    with pytest.raises(mla.MLAError):
+        mla.mla_mfma_rate(ops[: (1 << 17) - 8], 4, 16)  # below 256 KiB
+    with pytest.raises(mla.MLAError):
+        mla.mla_mfma_rate(ops, 4, 8)  # no such shape
+    with pytest.raises(mla.MLAError):
+        mla.mla_mfma_rate(ops, 0, 16)
