@@ -216,13 +216,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // and this kernel ran 2-9 % faster with it than with 32 x 32 x 16 tiles.
 // K moves in slices of 32 through a ring of four LDS stages
 // filled by direct-to-LDS buffer loads (three slices in flight).  Each 64-byte
-// tile row keeps its four 16-byte chunks at chunk ^ ((row >> 2) & 3): a
-// 16-byte fragment read serves 16 lanes (16 consecutive tile rows, one chunk
-// each) per pass over the LDS's 64 four-byte banks, and rows r, r + 4, r + 8,
-// r + 12 share a bank group unless their chunks differ, which this
-// permutation makes them do (with (row >> 1) & 3 rows r and r + 8 collided:
-// bank-conflict stalls of 8-14 % of the kernel time were counted).  The loads
-// apply the permutation on the global side.  The product is formed transposed
+// tile row keeps its four 16-byte chunks at chunk ^ ((row >> 2) & 2).  The
+// LDS (64 banks of 4 bytes, so 16 bank groups of 16 bytes) serves a 16-byte
+// read in four passes of 16 lanes, two per half-wave, the half-wave's 4-lane
+// groups split by the parity of the group index (lanes 0-3, 12-15, 20-27 in
+// one pass, 4-11, 16-19, 28-31 in the other: measured pair by pair with a
+// probe that times reads where only two lanes address different rows of one
+// bank group).  A fragment read (lane (l16, q4): row l16, chunk q4) puts in
+// one pass rows r, r + 12 of chunk q4 and rows r + 4, r + 8 of chunk q4 ^ 1
+// (r < 4), and rows r, r + 4, r + 8, r + 12 share a bank group: the
+// permutation sends those four reads to four different chunks.  With
+// chunk ^ ((row >> 2) & 3) two of them met and every fragment read took
+// twice the LDS cycles (bank-conflict stalls of 8-14 % of the kernel time
+// were counted).  The loads apply the permutation on the global side.  The product is formed transposed
 // (C^T = B A^T) so each lane holds four consecutive output columns; the output
 // goes through LDS so that every store writes whole rows.
 constexpr int GB_BM = 256, GB_BK = 32, GB_NST = 4, GB_GM = 4;
@@ -282,17 +288,17 @@ void gemm_big_kernel(GemmArgs g) {
   const int64_t lda2 = g.lda * 2, ldb2 = g.ldb * 2;
   // Load i of wave w moves tile rows 16 (4 i + w) .. +15 (64 bytes each):
   // lane l writes LDS bytes 16 l of that 1 KB, i.e. row + l/4, slot l%4,
-  // holding the row's logical chunk (l%4) ^ ((l/16) & 3).
-  const int32_t va = (int32_t)((lane >> 2) * lda2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
-  const int32_t vb = (int32_t)((lane >> 2) * ldb2) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+  // holding the row's logical chunk (l%4) ^ ((l/16) & 2).
+  const int32_t va = (int32_t)((lane >> 2) * lda2) + 16 * ((lane & 3) ^ ((lane >> 4) & 2));
+  const int32_t vb = (int32_t)((lane >> 2) * ldb2) + 16 * ((lane & 3) ^ ((lane >> 4) & 2));
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
   // 16 x 16 x 32 MFMA fragments: lane (l16, q4) holds tile row R = base + l16
   // (16 rows per fragment), k 8 q4 .. 8 q4 + 7 of the slice, i.e. logical
-  // chunk q4 of the row, stored at q4 ^ ((R >> 2) & 3); the row bases are
+  // chunk q4 of the row, stored at q4 ^ ((R >> 2) & 2); the row bases are
   // multiples of 16, so the XOR term is the same for every fragment.
   const int ra = wm * 128 + l16, rb = wn * (BN / 2) + l16;
-  const uint32_t fa = ra * GB_ROW + 16 * (q4 ^ ((ra >> 2) & 3));            // + 16 i rows
-  const uint32_t fb = A_BYTES + rb * GB_ROW + 16 * (q4 ^ ((rb >> 2) & 3));  // + 16 j rows
+  const uint32_t fa = ra * GB_ROW + 16 * (q4 ^ ((ra >> 2) & 2));            // + 16 i rows
+  const uint32_t fb = A_BYTES + rb * GB_ROW + 16 * (q4 ^ ((rb >> 2) & 2));  // + 16 j rows
   u32x4 af[2][NI], bfr[2][NJ];  // fragments of two slices (the one in use, the next)
   f32x4 acc[NI][NJ];  // [m tile][n tile], C^T layout: lane holds columns 4 q4 .. +3 of row l16
 
