@@ -602,305 +602,6 @@ void fa_bf16_kernel(FaArgs a, int n_work) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Eight-wave form of the same work item: 8 waves of 32 queries, two waves per
-// SIMD, so one wave's MFMAs run while the other waits on its softmax chain,
-// an LDS return or a tile.  Waves 0-3 ("group A") take a tile step as
-// QK(t), softmax(t), PV(t); waves 4-7 ("group B", one on each SIMD beside a
-// group-A wave) as softmax(t), PV(t), QK(t+1), so the two waves of a SIMD
-// are in different phases (one mostly on the MFMA, the other on the VALU)
-// for most of the step.  A tile (k^C, k^R and v^C rows of 64 keys, 40 KB)
-// sits in one stage of a 4-stage ring (160 KB): during step t group A reads
-// tile t, group B tiles t and t+1, and tiles t+2, t+3 are in flight.  The
-// row sums are fp32 sums of the exponentials.
-constexpr int F8_STAGE = FA_KSTAGE + FA_VSTAGE;  // 40960 bytes: k^C, k^R, v^C rows
-constexpr int F8_NST = 4;                        // tile stages
-constexpr int F8_LDS = F8_NST * F8_STAGE;        // 163840 bytes
-constexpr int F8_DMA = 5;                        // 16-byte loads per thread per tile
-constexpr int F8_QW = 32;                        // queries per wave
-constexpr int F8_FW = 3;                         // fragments read ahead
-
-template <bool GRP_B>
-__device__ __forceinline__ void fa8_item(const FaArgs& a, const int work, const bool desc, const uint32_t smem_addr) {
-  constexpr bool grp_b = GRP_B;
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int H = a.H;
-  const int n_qg = (a.L + FA_QG - 1) / FA_QG;
-  const int q0 = (n_qg - 1 - work % n_qg) * FA_QG;
-  const int head = (work / n_qg) % H, b = work / n_qg / H;
-  // keys [0, start_pos + last query of the workgroup]; step t takes key tile
-  // t, or nt - 1 - t in descending order
-  const int kv_hi = a.start_pos + min(q0 + FA_QG, a.L);
-  const int nt = (kv_hi + FA_KT - 1) / FA_KT;
-  auto key_tile = [&](int t) { return desc ? nt - 1 - t : t; };
-  const float scale_log2 = a.scale * FA_LOG2E;
-  const int qpos0 = a.start_pos + q0 + F8_QW * wave;  // position of the wave's first query
-  // a tile some key of which is at or before the wave's last query
-  auto visible = [&](int t) { return key_tile(t) * FA_KT <= qpos0 + F8_QW - 1; };
-
-  // ---- tile loads (swizzles as in the four-wave form).  Load n of wave w:
-  // n = 0, 1: k^C rows 4 (8 n + w) ..; n = 2, 3: v^C rows 4 (8 (n - 2) + w) ..;
-  // n = 4: k^R rows 8 w ..
-  const int64_t krow_bytes = (int64_t)H * FA_DH * 2;
-  const int ldkr2 = a.ld_kr * 2;
-  const int32_t dkc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15));
-  const int32_t dvc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
-  const int32_t dkr = (lane >> 3) * ldkr2 + 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
-  int32_t voff[F8_DMA];
-#pragma unroll
-  for (int n = 0; n < F8_DMA; ++n)
-    voff[n] = n < 2   ? (int32_t)(4 * (8 * n + wave) * krow_bytes) + dkc
-              : n < 4 ? (int32_t)(4 * (8 * (n - 2) + wave) * krow_bytes) + dvc
-                      : 8 * wave * ldkr2 + dkr;
-  const int64_t key_base = (int64_t)b * a.kv_end;
-  struct TileSrc {
-    __amdgpu_buffer_rsrc_t rk, rv, rr;
-    uint32_t st;
-  };
-  auto tile_src = [&](int t) {
-    const int kt = key_tile(t);
-    const int kb0 = max(kt, 0) * FA_KT;
-    const int rows = kt < 0 ? 0 : max(0, min(FA_KT, kv_hi - kb0));
-    TileSrc ts;
-    const int32_t nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
-    const int32_t nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
-    ts.rk = fa_rsrc(fa_uniform((const unsigned char*)a.kc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
-    ts.rv = fa_rsrc(fa_uniform((const unsigned char*)a.vc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
-    ts.rr = fa_rsrc(fa_uniform((const unsigned char*)a.kr + (key_base + kb0) * ldkr2), nb_r);
-    ts.st = __builtin_amdgcn_readfirstlane(smem_addr + (t % F8_NST) * F8_STAGE);
-    return ts;
-  };
-  auto issue_tile = [&](int t) {
-    const TileSrc ts = tile_src(t);
-    fa_dma16(ts.rk, ts.st + wave * 1024, voff[0]);
-    fa_dma16(ts.rk, ts.st + (8 + wave) * 1024, voff[1]);
-    fa_dma16(ts.rv, ts.st + FA_KSTAGE + wave * 1024, voff[2]);
-    fa_dma16(ts.rv, ts.st + FA_KSTAGE + (8 + wave) * 1024, voff[3]);
-    fa_dma16(ts.rr, ts.st + FA_KR + wave * 1024, voff[4]);
-  };
-  issue_tile(0);
-  issue_tile(1);
-
-  // ---- Q^T fragments of the wave's 32 queries (B operand of S^T = K Q^T):
-  // k step s covers dims 16 s .. 16 s + 15 (s < 8: q^C, s >= 8: q^R).
-  // Queries past L load as zero.
-  u32x4 qf[12];
-  {
-    const int t0 = q0 + F8_QW * wave;
-    const int nq = max(0, min(F8_QW, a.L - t0));
-    const int64_t row0 = (int64_t)b * a.L + t0;
-    const __amdgpu_buffer_rsrc_t rq = fa_rsrc(fa_uniform((const bf16*)a.qc + row0 * H * FA_DH + head * FA_DH),
-                                              nq > 0 ? (int32_t)((nq - 1) * krow_bytes + FA_DH * 2) : 0);
-    const __amdgpu_buffer_rsrc_t rr = fa_rsrc(fa_uniform((const bf16*)a.qr + row0 * H * FA_DR + head * FA_DR),
-                                              nq > 0 ? (nq - 1) * H * FA_DR * 2 + FA_DR * 2 : 0);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = fa_ld16(rq, (int32_t)(l32 * krow_bytes) + 32 * s + 16 * hi);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[8 + s] = fa_ld16(rr, l32 * H * FA_DR * 2 + 32 * s + 16 * hi);
-  }
-  issue_tile(2);
-
-  // Per-lane LDS read addresses (as in the four-wave form), relative to a
-  // stage: k^C fragment s of key block kb at (kx ^ 32 s) + kb 32 * 256, k^R
-  // fragment s at (rx ^ 32 s) + kb 32 * 128, V^T fragment (ks, d) from the
-  // transposing reads at ((FA_KSTAGE + vx) ^ 64 d) + ks 16 * 256 and 8 rows on.
-  const int g1 = (lane >> 4) & 1, jl = lane & 15, rl = 4 * hi + (jl >> 2);
-  const uint32_t kx = l32 * 256 + 16 * (hi ^ (l32 & 1)) + 32 * ((l32 & 15) >> 1);
-  const uint32_t rx = FA_KR + l32 * 128 + 16 * (hi ^ ((l32 >> 1) & 1)) + 32 * (((l32 >> 1) & 7) >> 1);
-  const uint32_t vx = rl * 256 + 64 * (rl & 3) + 32 * g1 + 16 * ((jl & 3) >> 1) + 8 * (jl & 1);
-
-  f32x16 acc[4];  // O^T [dim block of 32], queries on N
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[d][i] = 0.f;
-  // running max (log2 units, finite floor: a row whose first tiles are all
-  // masked gets p = 0 there) and this lane's half of the row sum
-  float m_run = -1e30f, l_run = 0.f;
-
-  // S^T = K Q^T for tile t: key block kb (32 keys) on M, the wave's queries
-  // on N.  Every operand and accumulator is in VGPRs (with AGPRs in use the
-  // compiler gives each file half of the wave's 256 registers, and the
-  // query fragments spilled).  MFMAs from asm, so the wait states before the
-  // VALU reads an MFMA result are given explicitly.
-  // Fragments are read F8_FW MFMAs ahead through a small ring of registers
-  // (left to itself the compiler reads a whole product's fragments at once).
-  auto qk = [&](int t, f32x16 (&s)[2]) {
-    const uint32_t kq = smem_addr + (t % F8_NST) * F8_STAGE + kx;
-    const uint32_t rq = smem_addr + (t % F8_NST) * F8_STAGE + rx;
-    auto load = [&](auto G) -> u32x4 {  // fragment g: k step g / 2, key block g % 2
-      constexpr int g = decltype(G)::value, st = g / 2, kb = g % 2;
-      if constexpr (st < 8)
-        return fa_lds16((kq ^ (32 * st)) + kb * 32 * 256);
-      else
-        return fa_lds16((rq ^ (32 * (st - 8))) + kb * 32 * 128);
-    };
-    u32x4 fr[F8_FW + 1];
-    static_for<F8_FW>([&](auto G) { fr[decltype(G)::value] = load(G); });
-    static_for<24>([&](auto J) {
-      constexpr int j = decltype(J)::value, st = j / 2, kb = j % 2;
-      if constexpr (j + F8_FW < 24) fr[(j + F8_FW) % (F8_FW + 1)] = load(std::integral_constant<int, j + F8_FW>{});
-      if constexpr (st == 0)
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s[kb]) : "v"(fr[j % (F8_FW + 1)]), "v"(qf[st]));
-      else
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s[kb]) : "v"(fr[j % (F8_FW + 1)]), "v"(qf[st]));
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
-  };
-  // softmax of tile t (scores s), then O^T += V^T P^T
-  auto softmax_pv = [&](int t, f32x16 (&s)[2]) {
-    const int kt = key_tile(t);
-    if (kt * FA_KT + FA_KT - 1 > qpos0) {
-      // on the diagonal: register i of key block kb holds key kt 64 + 32 kb +
-      // 8 (i/4) + 4 hi + i%4, masked for query qpos0 + l32 when later
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) fa_causal_mask(s[kb], qpos0 + l32 - kt * FA_KT - 32 * kb - 4 * hi);
-    }
-    float m4[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) m4[c] = fa_max3(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1], s[c >> 1][8 * (c & 1) + 2]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 3; i < 8; i += 2) {
-        const int kb = c >> 1, o = 8 * (c & 1);
-        m4[c] = i + 1 < 8 ? fa_max3(m4[c], s[kb][o + i], s[kb][o + i + 1]) : fa_max3(m4[c], s[kb][o + i], s[kb][o + i]);
-      }
-    float mx = fa_max3(fa_max3(m4[0], m4[1], m4[2]), m4[3], m4[3]);
-    {  // the other half of the query's keys is in lane l ^ 32
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fa_max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1])) * scale_log2;
-    }
-    // the running max is raised only when the tile max exceeds it by more
-    // than FA_SLACK (p <= 2^8 stays exact in fp32); from the floor, the first
-    // tile with a visible key raises it, with alpha = 2^(-1e30 - m) = 0
-    const bool need = __any(mx > m_run + FA_SLACK);
-    const float mh = need ? fmaxf(mx, m_run) : m_run;
-    if (need) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mh);
-      // (the last MFMA that wrote acc is a whole QK product back at least)
-      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-#pragma unroll
-      for (int d = 0; d < 4; ++d) acc[d] *= alpha;
-      l_run *= alpha;
-    }
-    m_run = mh;
-    // P^T for key step ks = 2 kb + h2 (16 keys): registers 8 h2 .. 8 h2 + 7
-    // of key block kb, packed in pairs
-    u32x4 p[4];
-    float lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int kb = k >> 3, h2 = (k >> 2) & 1, e = k & 3, i = 8 * h2 + 2 * e;
-      const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, -mh));
-      const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], scale_log2, -mh));
-      lt += ea + eb;
-      p[2 * kb + h2][e] = pack_bf16x2(ea, eb);
-    }
-    l_run += lt;
-    const uint32_t vq = smem_addr + (t % F8_NST) * F8_STAGE + FA_KSTAGE + vx;
-    auto load = [&](auto G) -> u32x4 {  // fragment g: key step g / 4, dim block g % 4
-      constexpr int g = decltype(G)::value, ks = g / 4, d = g % 4;
-      const uint32_t vb = (vq ^ (64 * d)) + ks * 16 * 256;
-      const u32x2 lo = fa_tr16(vb), hv = fa_tr16(vb + 8 * 256);
-      return u32x4{lo[0], lo[1], hv[0], hv[1]};
-    };
-    u32x4 fr[F8_FW + 1];
-    static_for<F8_FW>([&](auto G) { fr[decltype(G)::value] = load(G); });
-    static_for<16>([&](auto J) {
-      constexpr int j = decltype(J)::value, ks = j / 4, d = j % 4;
-      if constexpr (j + F8_FW < 16) fr[(j + F8_FW) % (F8_FW + 1)] = load(std::integral_constant<int, j + F8_FW>{});
-      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[d]) : "v"(fr[j % (F8_FW + 1)]), "v"(p[ks]));
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-
-  fa_wait_vmcnt<F8_DMA>();  // tiles 0 and 1 (and the queries) have landed
-  __syncthreads();
-  f32x16 sc[2];  // scores; in group B, those of the next tile between steps
-  if constexpr (grp_b)
-    if (visible(0)) qk(0, sc);
-  for (int t = 0; t < nt; ++t) {
-    issue_tile(t + 3);  // into the stage of tile t - 1, which no wave reads any more
-    if constexpr (!grp_b) {
-      if (visible(t)) {
-        qk(t, sc);
-        softmax_pv(t, sc);
-      }
-    } else {
-      if (visible(t)) softmax_pv(t, sc);
-      if (t + 1 < nt && visible(t + 1)) qk(t + 1, sc);
-    }
-    fa_wait_vmcnt<F8_DMA>();  // tile t + 2 has landed (t + 3 in flight)
-    __syncthreads();
-  }
-  fa_wait_vmcnt<0>();  // tiles past the end still write LDS: drain them
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-
-  // ---- out[t][head][:] = O^T[:, t] / l.  Lane (l32, hi), tuple d, register
-  // 4g + e: dim 32 d + 8 g + 4 hi + e of query l32; lanes l and l + 32 trade
-  // halves (v_permlane32_swap) so each stores 8 whole dims.
-  const int tq = q0 + F8_QW * wave + l32;
-  const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float inv = 1.f / (__uint_as_float(lr[0]) + __uint_as_float(lr[1]));
-  if (tq < a.L) {
-    bf16* o = (bf16*)a.out + (((int64_t)b * a.L + tq) * H + head) * FA_DH;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        uint32_t own[2][2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int g = 2 * gp + k;
-          own[k][0] = pack_bf16x2(acc[d][4 * g] * inv, acc[d][4 * g + 1] * inv);
-          own[k][1] = pack_bf16x2(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
-        }
-        u32x4 v;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const auto r = __builtin_amdgcn_permlane32_swap(own[0][e], own[1][e], false, false);
-          v[e] = r[0];
-          v[2 + e] = r[1];
-        }
-        *reinterpret_cast<u32x4*>(o + 32 * d + 8 * (2 * gp + hi)) = v;
-      }
-  }
-}
-
-// Persistent workgroups of the eight-wave form, scheduled as fa_bf16_kernel.
-// Each group runs its own instance of the item loop (one loop body holding
-// both orders needed more than the wave's 256 registers); both pass the same
-// barriers.
-template <bool GRP_B>
-__device__ __forceinline__ void fa8_rounds(const FaArgs& a, const int n_work, const uint32_t smem_addr) {
-  const int G = (int)gridDim.x, g = (int)blockIdx.x, x = g % 8, k = g / 8;
-  const int q = n_work / 8, r = n_work % 8;
-  const int n_x = q + (x < r ? 1 : 0), base = x * q + min(x, r);
-  const int P = (G - x + 7) / 8;
-  bool first = true;
-  for (int rd = 0; rd * P < n_x; ++rd) {
-    const int i = rd * P + ((rd & 1) ? P - 1 - k : k);
-    if (i >= n_x) continue;
-    if (!first) __syncthreads();
-    first = false;
-    fa8_item<GRP_B>(a, base + i, (rd & 1) != 0, smem_addr);
-  }
-}
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa8_bf16_kernel(FaArgs a, int n_work) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[F8_LDS];
-  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-  if (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) >= 4)
-    fa8_rounds<true>(a, n_work, smem_addr);
-  else
-    fa8_rounds<false>(a, n_work, smem_addr);
-}
-
 // Rows [0, kv_end) of every sequence from the paged cache into a contiguous
 // [B * kv_end, row] buffer (one 16-byte chunk per thread); a block-table entry
 // outside the pool gives zeros and sets err_flags.
@@ -951,7 +652,7 @@ hipError_t launch_fa_bf16(const FaArgs& a, hipStream_t st) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(n, std::max(cus, 8));  // one workgroup per CU
-  hipLaunchKernelGGL(fa8_bf16_kernel, dim3((unsigned)grid), dim3(512), 0, st, a, (int)n);
+  hipLaunchKernelGGL(fa_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, (int)n);
   return hipGetLastError();
 }
 
