@@ -497,10 +497,15 @@ def run_ceilings(steps: int = 20) -> dict:
         torch.cuda.synchronize()
         ms_m = float(np.median([ev.elapsed_ms(i) for i in range(steps)]))
         ev.close()
+        # the core clock under the stream (s_memtime cycles per 100 MHz tick)
+        clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+        mla.mla_mfma_rate(ops, iters, shape, clocks=clk)
+        cyc, ticks = (int(v) for v in clk.tolist())
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         tf = cus * 4 * iters * 2 ** 20 / (ms_m * 1e-3) / 1e12
         mf[f"tflops_{shape}x{shape}"] = round(tf, 1)
         mf[f"frac_of_spec_{shape}x{shape}"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        mf[f"clock_ghz_{shape}x{shape}"] = round(0.1 * cyc / ticks, 3) if ticks > 0 else None
     res["mfma_bf16"] = mf
     del ops
     # The vendor GEMM library (torch.mm) on the same operands and layout

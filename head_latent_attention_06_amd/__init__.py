@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
             "mla_decode_num_splits": (I32, [CP, I32, I32, I32]),
             "mla_decode_noalloc": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P]),
             "mla_stream_read": (I32, [P, ctypes.c_int64, P, P]),
-            "mla_mfma_rate": (I32, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P]),
+            "mla_mfma_rate": (I32, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]),
             "mla_decode_profiled": (I32, [CP, KP, P, I32, I32, I32, P, P, P, P, P, P, SZ, P, P, P]),
             "mla_prefill_profiled": (I32, [CP, KP, WP, P, I32, I32, I32, P, P, SZ, P, P, P]),
             "mla_output_projection_workspace_size": (I32, [CP, I32, I32, ctypes.POINTER(SZ)]),
@@ -398,19 +398,26 @@ def mla_decode(cfg: Config, cache: PagedCache, kv_lens, max_kv_len: int, q_nope,
         _check(lib().mla_decode_profiled(*args, *attn_events), where)
 
 
-def mla_mfma_rate(operands, iters: int, shape: int = 16, sink=None, stream=None) -> None:
+def mla_mfma_rate(operands, iters: int, shape: int = 16, sink=None, clocks=None, stream=None) -> None:
     """A stream of independent MFMAs on all CUs (2^20 FLOP per wave per
     round, `iters` rounds, one workgroup of four waves per CU) with operand
     fragments taken from `operands` (a contiguous GPU bf16 tensor of at least
     256 KiB): the sustained matrix-core rate.  shape 16 or 32 picks the
-    16x16x32 or the 32x32x16 instruction."""
+    16x16x32 or the 32x32x16 instruction.  clocks (optional, a zeroed GPU
+    int64 tensor of 2 elements) receives the core-clock cycles and 100 MHz
+    ticks the workgroups spent in their MFMA rounds."""
     where = "mla_mfma_rate"
     _tensor(where, "operands", operands, torch.bfloat16)
     if sink is not None:
         _tensor(where, "sink", sink, torch.float32)
-    _on_gpu(where, operands=operands, sink=sink)
+    if clocks is not None:
+        _tensor(where, "clocks", clocks, torch.int64)
+        if clocks.numel() < 2:
+            _bad(where, "clocks needs 2 elements")
+    _on_gpu(where, operands=operands, sink=sink, clocks=clocks)
     _check(lib().mla_mfma_rate(_ptr(operands), operands.numel() * 2, int(iters), int(shape),
-                               None if sink is None else _ptr(sink), _stream(stream)), where)
+                               None if sink is None else _ptr(sink), None if clocks is None else _ptr(clocks),
+                               _stream(stream)), where)
 
 
 def mla_stream_read(src, sink=None, stream=None) -> None:

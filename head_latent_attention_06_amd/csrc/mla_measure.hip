@@ -61,11 +61,17 @@ constexpr int MR_FRAGS = 16;  // 16-byte operand fragments per lane (A and B)
 // (two passes over 16 accumulators), no MFMA depending on the one before.
 template <int SHAPE>
 __global__ __launch_bounds__(256) void mfma_rate_kernel(const u32x4* __restrict__ ops, int64_t n16, int iters,
-                                                        float* __restrict__ sink) {
+                                                        float* __restrict__ sink,
+                                                        unsigned long long* __restrict__ clocks) {
   const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * MR_FRAGS;
   u32x4 f[MR_FRAGS];
 #pragma unroll
   for (int k = 0; k < MR_FRAGS; ++k) f[k] = ops[(base + k) % n16];
+  // core-clock and 100 MHz counters around the MFMA rounds (the empty asm
+  // keeps the MFMAs, which read f, after the first pair of reads)
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll
+  for (int k = 0; k < MR_FRAGS; ++k) asm volatile("" : "+v"(f[k]));
   float total = 0.f;
   if constexpr (SHAPE == 16) {
     f32x4 acc[64];
@@ -104,6 +110,12 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(const u32x4* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; ++e) total += acc[i][e];
   }
+  asm volatile("" : "+v"(total));
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (clocks && threadIdx.x == 0) {
+    atomicAdd(&clocks[0], (unsigned long long)(c1 - c0));
+    atomicAdd(&clocks[1], (unsigned long long)(r1 - r0));
+  }
   if (total == 1234567.0f && sink) sink[0] = total;
 }
 
@@ -124,8 +136,9 @@ extern "C" mla_status mla_stream_read(const void* src, int64_t bytes, void* sink
 }
 
 extern "C" mla_status mla_mfma_rate(const void* operands, int64_t bytes, int32_t iters, int32_t shape, void* sink,
-                                   void* stream) {
-  if (!operands || bytes < 262144 || ((uintptr_t)operands & 15) || iters <= 0 || (shape != 16 && shape != 32))
+                                   void* clocks, void* stream) {
+  if (!operands || bytes < 262144 || ((uintptr_t)operands & 15) || iters <= 0 || (shape != 16 && shape != 32) ||
+      ((uintptr_t)clocks & 7))
     return MLA_ERR_INVALID_ARG;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -134,9 +147,9 @@ extern "C" mla_status mla_mfma_rate(const void* operands, int64_t bytes, int32_t
   const int64_t n16 = bytes / 16;
   if (shape == 16)
     hipLaunchKernelGGL(mla::mfma_rate_kernel<16>, dim3((unsigned)cus), dim3(256), 0, (hipStream_t)stream,
-                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink);
+                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink, (unsigned long long*)clocks);
   else
     hipLaunchKernelGGL(mla::mfma_rate_kernel<32>, dim3((unsigned)cus), dim3(256), 0, (hipStream_t)stream,
-                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink);
+                       (const mla::u32x4*)operands, n16, (int)iters, (float*)sink, (unsigned long long*)clocks);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -293,9 +293,15 @@ mla_status mla_stream_read(const void* src, int64_t bytes, void* sink, void* str
  * end wrap around), iters > 0, shape 16 or 32, else MLA_ERR_INVALID_ARG.
  * `sink` (may be NULL, else one writable float) is written only in the
  * practically impossible case that the accumulators' sum is exactly
- * 1234567.0. */
+ * 1234567.0.  `clocks` (may be NULL, else two 8-byte-aligned uint64 on the
+ * device, which the caller zeroes) receives, summed over the workgroups,
+ * the core-clock cycles (s_memtime) and the 100 MHz ticks (s_memrealtime)
+ * each spent in its MFMA rounds: 0.1 * clocks[0] / clocks[1] is the average
+ * core clock in GHz under the stream (the matrix cores run at the part's
+ * power limit, below the 2.4 GHz peak clock).  A misaligned clocks pointer
+ * gives MLA_ERR_INVALID_ARG. */
 mla_status mla_mfma_rate(const void* operands, int64_t bytes, int32_t iters, int32_t shape, void* sink,
-                         void* stream);
+                         void* clocks, void* stream);
 
 /* Upper bound on the attention work items (split partial slots) mla_decode
  * plans for these sizes; the device plan cuts each query row's visible keys

@@ -65,6 +65,18 @@ def test_mfma_rate_runs_and_rejects_bad_arguments():
         mla.mla_mfma_rate(ops, 4, shape, sink)
     torch.cuda.synchronize()
     assert float(sink.item()) == 0.0  # the accumulators' sum is not the magic value
+    # clock counters: 200 rounds are thousands of core cycles per workgroup,
+    # and the core clock lies between 0.5 GHz and the 2.4 GHz peak
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for shape in (16, 32):
+        clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+        mla.mla_mfma_rate(ops, 200, shape, clocks=clk)
+        torch.cuda.synchronize()
+        cyc, ticks = (int(v) for v in clk.tolist())
+        assert cyc > cus * 1000 and ticks > 0
+        assert 0.5 <= 0.1 * cyc / ticks <= 2.5
+    with pytest.raises(mla.MLAError):
+        mla.mla_mfma_rate(ops, 4, 16, clocks=torch.zeros(1, dtype=torch.int64, device="cuda"))
     with pytest.raises(mla.MLAError):
         mla.mla_mfma_rate(ops[: (1 << 17) - 8], 4, 16)  # below 256 KiB
     with pytest.raises(mla.MLAError):
