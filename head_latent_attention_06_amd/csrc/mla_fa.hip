@@ -602,349 +602,6 @@ void fa_bf16_kernel(FaArgs a, int n_work) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// The same work item on v_mfma_f32_16x16x32_bf16, which the part runs at a
-// higher clock than the 32 x 32 x 16 instruction for the same work (all-CU
-// MFMA streams on random operands: 2.14 against 1.86 GHz, both at ~94 % of
-// the per-clock peak), and this kernel is bound by that clock.  8 waves of
-// 32 queries, two waves per SIMD (waves w and w + 4 share one); waves 0-3
-// ("group A") take a tile step as QK(t), softmax(t), PV(t), waves 4-7
-// ("group B") as softmax(t), PV(t), QK(t+1), so the two waves of a SIMD are
-// mostly in different phases.  A tile (k^C, k^R and v^C rows of 64 keys,
-// 40 KB) sits in one stage of a 4-stage ring (160 KB): during step t group
-// A reads tile t, group B tiles t and t+1, and tiles t+2, t+3 are in flight.
-// 16 x 16 layouts (lane l = 16 q4 + l16): an A fragment holds row l16 and
-// k 8 q4 .. 8 q4 + 7 of a 16 x 32 block, a B fragment column l16 and the
-// same k, a result tile row 4 q4 + e and column l16.  So S^T (keys on M,
-// queries on N) leaves each lane 16 keys of two queries, the four lanes
-// l16 + 16 q4 sharing a query's 64 keys; P^T of key step ks (32 keys) holds
-// keys 32 ks + 4 q4 + j and 32 ks + 16 + 4 q4 + j (j < 4), and the
-// transposing V reads produce V^T fragments in that key order.  Every
-// operand and accumulator is in VGPRs (with AGPRs in use the compiler gives
-// each file half of the wave's 256 registers); MFMAs are issued from asm,
-// with the wait states before a VALU read of their results written out.
-constexpr int F16_STAGE = FA_KSTAGE + FA_VSTAGE;  // 40960 bytes: k^C, k^R, v^C rows
-constexpr int F16_NST = 4;                        // tile stages
-constexpr int F16_LDS = F16_NST * F16_STAGE;        // 163840 bytes
-constexpr int F16_DMA = 5;                        // 16-byte loads per thread per tile
-constexpr int F16_QW = 32;                        // queries per wave
-constexpr int F16_FW = 3;                         // fragments read ahead
-
-template <bool GRP_B>
-__device__ __forceinline__ void fa16_item(const FaArgs& a, const int work, const bool desc, const uint32_t smem_addr) {
-  constexpr bool grp_b = GRP_B;
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  (void)lane;
-  const int H = a.H;
-  const int n_qg = (a.L + FA_QG - 1) / FA_QG;
-  const int q0 = (n_qg - 1 - work % n_qg) * FA_QG;
-  const int head = (work / n_qg) % H, b = work / n_qg / H;
-  // keys [0, start_pos + last query of the workgroup]; step t takes key tile
-  // t, or nt - 1 - t in descending order
-  const int kv_hi = a.start_pos + min(q0 + FA_QG, a.L);
-  const int nt = (kv_hi + FA_KT - 1) / FA_KT;
-  auto key_tile = [&](int t) { return desc ? nt - 1 - t : t; };
-  const float scale_log2 = a.scale * FA_LOG2E;
-  const int qpos0 = a.start_pos + q0 + F16_QW * wave;  // position of the wave's first query
-  // a tile some key of which is at or before the wave's last query
-  auto visible = [&](int t) { return key_tile(t) * FA_KT <= qpos0 + F16_QW - 1; };
-
-  // ---- tile loads (swizzles as in the four-wave form).  Load n of wave w:
-  // n = 0, 1: k^C rows 4 (8 n + w) ..; n = 2, 3: v^C rows 4 (8 (n - 2) + w) ..;
-  // n = 4: k^R rows 8 w ..
-  const int64_t krow_bytes = (int64_t)H * FA_DH * 2;
-  const int ldkr2 = a.ld_kr * 2;
-  const int32_t dkc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15));
-  const int32_t dvc = (int32_t)((lane >> 4) * krow_bytes) + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
-  const int32_t dkr = (lane >> 3) * ldkr2 + 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
-  int32_t voff[F16_DMA];
-#pragma unroll
-  for (int n = 0; n < F16_DMA; ++n)
-    voff[n] = n < 2   ? (int32_t)(4 * (8 * n + wave) * krow_bytes) + dkc
-              : n < 4 ? (int32_t)(4 * (8 * (n - 2) + wave) * krow_bytes) + dvc
-                      : 8 * wave * ldkr2 + dkr;
-  const int64_t key_base = (int64_t)b * a.kv_end;
-  struct TileSrc {
-    __amdgpu_buffer_rsrc_t rk, rv, rr;
-    uint32_t st;
-  };
-  auto tile_src = [&](int t) {
-    const int kt = key_tile(t);
-    const int kb0 = max(kt, 0) * FA_KT;
-    const int rows = kt < 0 ? 0 : max(0, min(FA_KT, kv_hi - kb0));
-    TileSrc ts;
-    const int32_t nb_kv = __builtin_amdgcn_readfirstlane(rows > 0 ? (int32_t)((rows - 1) * krow_bytes + FA_DH * 2) : 0);
-    const int32_t nb_r = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * ldkr2 + FA_DR * 2 : 0);
-    ts.rk = fa_rsrc(fa_uniform((const unsigned char*)a.kc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
-    ts.rv = fa_rsrc(fa_uniform((const unsigned char*)a.vc + ((key_base + kb0) * H * FA_DH + head * FA_DH) * 2), nb_kv);
-    ts.rr = fa_rsrc(fa_uniform((const unsigned char*)a.kr + (key_base + kb0) * ldkr2), nb_r);
-    ts.st = __builtin_amdgcn_readfirstlane(smem_addr + (t % F16_NST) * F16_STAGE);
-    return ts;
-  };
-  auto issue_tile = [&](int t) {
-    const TileSrc ts = tile_src(t);
-    fa_dma16(ts.rk, ts.st + wave * 1024, voff[0]);
-    fa_dma16(ts.rk, ts.st + (8 + wave) * 1024, voff[1]);
-    fa_dma16(ts.rv, ts.st + FA_KSTAGE + wave * 1024, voff[2]);
-    fa_dma16(ts.rv, ts.st + FA_KSTAGE + (8 + wave) * 1024, voff[3]);
-    fa_dma16(ts.rr, ts.st + FA_KR + wave * 1024, voff[4]);
-  };
-  issue_tile(0);
-  issue_tile(1);
-
-  // ---- Q^T fragments (B operand of S^T = K Q^T): query tile n (16 queries),
-  // k step s covers dims 32 s + 8 q4 .. + 7 (s < 4: q^C, s >= 4: q^R).
-  // Queries past L load as zero.
-  const int l16 = lane & 15, q4 = lane >> 4;
-  u32x4 qf[2][6];
-  {
-    const int t0 = q0 + F16_QW * wave;
-    const int nq = max(0, min(F16_QW, a.L - t0));
-    const int64_t row0 = (int64_t)b * a.L + t0;
-    const __amdgpu_buffer_rsrc_t rq = fa_rsrc(fa_uniform((const bf16*)a.qc + row0 * H * FA_DH + head * FA_DH),
-                                              nq > 0 ? (int32_t)((nq - 1) * krow_bytes + FA_DH * 2) : 0);
-    const __amdgpu_buffer_rsrc_t rr = fa_rsrc(fa_uniform((const bf16*)a.qr + row0 * H * FA_DR + head * FA_DR),
-                                              nq > 0 ? (nq - 1) * H * FA_DR * 2 + FA_DR * 2 : 0);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qf[n][s] = fa_ld16(rq, (int32_t)((16 * n + l16) * krow_bytes) + 64 * s + 16 * q4);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) qf[n][4 + s] = fa_ld16(rr, (16 * n + l16) * H * FA_DR * 2 + 64 * s + 16 * q4);
-    }
-  }
-  issue_tile(2);
-
-  // Per-lane LDS read addresses, relative to a stage (chunk swizzles of the
-  // tile loads: k^C chunk c of row r at c ^ (r & 15), k^R at c ^ ((r >> 1) & 7),
-  // v^C at c ^ 4 (r & 3)):
-  //   k^C fragment (m, s < 4): row 16 m + l16, chunk 4 s + q4:
-  //       (kx ^ 64 s) + m 16 * 256
-  //   k^R fragment (m, s >= 4): row 16 m + l16, chunk 4 (s - 4) + q4:
-  //       (rx ^ 64 (s - 4)) + m 16 * 128
-  //   V^T fragment (ks, d), read h: source lane l16 = 4 k + a gives dims
-  //       16 d + 4 a .. + 3 of key row 32 ks + 16 h + 4 q4 + k:
-  //       (FA_KSTAGE + vx ^ 32 d) + (32 ks + 16 h) * 256
-  // (the stage bases are multiples of 256, so the XORs act on the per-lane
-  // part only).
-  const uint32_t kx = l16 * 256 + 16 * (q4 ^ l16);
-  const uint32_t rx = FA_KR + l16 * 128 + 16 * (q4 ^ (l16 >> 1));
-  const int va_ = l16 & 3, vk = l16 >> 2;
-  const uint32_t vx = (4 * q4 + vk) * 256 + 16 * ((va_ >> 1) ^ (4 * vk)) + 8 * (va_ & 1);
-
-  f32x4 acc[8][2];  // O^T [dim tile of 16][query tile]
-#pragma unroll
-  for (int d = 0; d < 8; ++d)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) acc[d][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max per query tile (log2 units, finite floor: a row whose first
-  // tiles are all masked gets p = 0 there) and this lane's part of the row sum
-  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
-
-  // S^T = K Q^T for tile t: s[m][n] is keys 16 m .., queries 16 n ..
-  auto qk = [&](int t, f32x4 (&sc)[4][2]) {
-    const uint32_t st = smem_addr + (t % F16_NST) * F16_STAGE;
-    auto load = [&](auto G) -> u32x4 {  // fragment g: k step g / 4, key tile g % 4
-      constexpr int g = decltype(G)::value, s = g / 4, m = g % 4;
-      if constexpr (s < 4)
-        return fa_lds16(((st + kx) ^ (64 * s)) + m * 16 * 256);
-      else
-        return fa_lds16(((st + rx) ^ (64 * (s - 4))) + m * 16 * 128);
-    };
-    u32x4 fr[F16_FW + 1];
-    static_for<F16_FW>([&](auto G) { fr[decltype(G)::value] = load(G); });
-    static_for<24>([&](auto J) {
-      constexpr int j = decltype(J)::value, s = j / 4, m = j % 4;
-      if constexpr (j + F16_FW < 24) fr[(j + F16_FW) % (F16_FW + 1)] = load(std::integral_constant<int, j + F16_FW>{});
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        if constexpr (s == 0)
-          asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(sc[m][n]) : "v"(fr[j % (F16_FW + 1)]), "v"(qf[n][s]));
-        else
-          asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(sc[m][n]) : "v"(fr[j % (F16_FW + 1)]), "v"(qf[n][s]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(sc[0][0]), "+v"(sc[0][1]), "+v"(sc[1][0]), "+v"(sc[1][1]), "+v"(sc[2][0]), "+v"(sc[2][1]),
-                   "+v"(sc[3][0]), "+v"(sc[3][1]));
-  };
-  // max / sum of a per-query value over the four lanes l16 + 16 q4
-  auto rows_max = [&](float x) {
-    const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = fmaxf(__uint_as_float(r1[0]), __uint_as_float(r1[1]));
-    const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
-  };
-  auto rows_sum = [&](float x) {
-    const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
-    const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
-  };
-  // softmax of tile t (scores sc), then O^T += V^T P^T
-  auto softmax_pv = [&](int t, f32x4 (&sc)[4][2]) {
-    const int kt = key_tile(t);
-    if (kt * FA_KT + FA_KT - 1 > qpos0) {
-      // on the diagonal: sc[m][n][e] is key kt 64 + 16 m + 4 q4 + e, query
-      // qpos0 + 16 n + l16; masked when the key is later
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int thr = qpos0 + 16 * n + l16 - kt * FA_KT - 4 * q4;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[m][n][e] = 16 * m + e > thr ? -INFINITY : sc[m][n][e];
-      }
-    }
-    float mh[2];
-    bool need[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float x = fa_max3(sc[0][n][0], sc[0][n][1], sc[0][n][2]);
-      x = fa_max3(x, sc[0][n][3], sc[1][n][0]);
-      x = fa_max3(x, sc[1][n][1], sc[1][n][2]);
-      x = fa_max3(x, sc[1][n][3], sc[2][n][0]);
-      x = fa_max3(x, sc[2][n][1], sc[2][n][2]);
-      x = fa_max3(x, sc[2][n][3], sc[3][n][0]);
-      x = fa_max3(x, sc[3][n][1], sc[3][n][2]);
-      x = fa_max3(x, sc[3][n][3], sc[3][n][3]);
-      const float mx = rows_max(x) * scale_log2;
-      // the running max is raised only when the tile max exceeds it by more
-      // than FA_SLACK (p <= 2^8 stays exact in fp32); from the floor, the
-      // first tile with a visible key raises it, with alpha = 2^(-1e30 - m) = 0
-      need[n] = __any(mx > m_run[n] + FA_SLACK);
-      mh[n] = need[n] ? fmaxf(mx, m_run[n]) : m_run[n];
-    }
-    if (need[0] || need[1]) {
-      // (the last MFMA that wrote acc is a whole QK product back at least)
-      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        if (need[n]) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[n] - mh[n]);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[d][n] *= alpha;
-          l_run[n] *= alpha;
-        }
-    }
-    // P^T of key step ks: keys 32 ks + 4 q4 + j (key tile 2 ks) and
-    // 32 ks + 16 + 4 q4 + j (key tile 2 ks + 1), j < 4, packed in pairs
-    u32x4 p[2][2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      m_run[n] = mh[n];
-      float lt = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float e4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          e4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[m][n][e], scale_log2, -mh[n]));
-          lt += e4[e];
-        }
-        p[m >> 1][n][2 * (m & 1)] = pack_bf16x2(e4[0], e4[1]);
-        p[m >> 1][n][2 * (m & 1) + 1] = pack_bf16x2(e4[2], e4[3]);
-      }
-      l_run[n] += lt;
-    }
-    const uint32_t vq = smem_addr + (t % F16_NST) * F16_STAGE + FA_KSTAGE + vx;
-    auto load = [&](auto G) -> u32x4 {  // fragment g: key step g / 8, dim tile g % 8
-      constexpr int g = decltype(G)::value, ks = g / 8, d = g % 8;
-      const uint32_t vb = (vq ^ (32 * d)) + ks * 32 * 256;
-      const u32x2 lo = fa_tr16(vb), hv = fa_tr16(vb + 16 * 256);
-      return u32x4{lo[0], lo[1], hv[0], hv[1]};
-    };
-    u32x4 fr[F16_FW + 1];
-    static_for<F16_FW>([&](auto G) { fr[decltype(G)::value] = load(G); });
-    static_for<16>([&](auto J) {
-      constexpr int j = decltype(J)::value, ks = j / 8, d = j % 8;
-      if constexpr (j + F16_FW < 16) fr[(j + F16_FW) % (F16_FW + 1)] = load(std::integral_constant<int, j + F16_FW>{});
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-            : "+v"(acc[d][n]) : "v"(fr[j % (F16_FW + 1)]), "v"(p[ks][n]));
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-
-  fa_wait_vmcnt<F16_DMA>();  // tiles 0 and 1 (and the queries) have landed
-  __syncthreads();
-  f32x4 sc[4][2];  // scores; in group B, those of the next tile between steps
-  if constexpr (grp_b)
-    if (visible(0)) qk(0, sc);
-  for (int t = 0; t < nt; ++t) {
-    issue_tile(t + 3);  // into the stage of tile t - 1, which no wave reads any more
-    if constexpr (!grp_b) {
-      if (visible(t)) {
-        qk(t, sc);
-        softmax_pv(t, sc);
-      }
-    } else {
-      if (visible(t)) softmax_pv(t, sc);
-      if (t + 1 < nt && visible(t + 1)) qk(t + 1, sc);
-    }
-    fa_wait_vmcnt<F16_DMA>();  // tile t + 2 has landed (t + 3 in flight)
-    __syncthreads();
-  }
-  fa_wait_vmcnt<0>();  // tiles past the end still write LDS: drain them
-  // wait states between the last MFMAs and the VALU reads of acc below
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[2][0]),
-                 "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]), "+v"(acc[4][0]), "+v"(acc[4][1]),
-                 "+v"(acc[5][0]), "+v"(acc[5][1]), "+v"(acc[6][0]), "+v"(acc[6][1]), "+v"(acc[7][0]),
-                 "+v"(acc[7][1]));
-
-  // ---- out[t][head][:] = O^T[:, t] / l.  Lane (l16, q4), tile (d, n),
-  // register e: dim 16 d + 4 q4 + e of query 16 n + l16 (8 bytes per store).
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int tq = q0 + F16_QW * wave + 16 * n + l16;
-    const float inv = 1.f / rows_sum(l_run[n]);
-    if (tq < a.L) {
-      bf16* o = (bf16*)a.out + (((int64_t)b * a.L + tq) * H + head) * FA_DH + 4 * q4;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const u32x2 v = {pack_bf16x2(acc[d][n][0] * inv, acc[d][n][1] * inv),
-                         pack_bf16x2(acc[d][n][2] * inv, acc[d][n][3] * inv)};
-        *reinterpret_cast<u32x2*>(o + 16 * d) = v;
-      }
-    }
-  }
-}
-
-// Persistent workgroups of the 16 x 16 form, scheduled as fa_bf16_kernel.
-// Each group runs its own instance of the item loop (one loop body holding
-// both orders needed more than the wave's 256 registers); both pass the same
-// barriers.
-template <bool GRP_B>
-__device__ __forceinline__ void fa16_rounds(const FaArgs& a, const int n_work, const uint32_t smem_addr) {
-  const int G = (int)gridDim.x, g = (int)blockIdx.x, x = g % 8, k = g / 8;
-  const int q = n_work / 8, r = n_work % 8;
-  const int n_x = q + (x < r ? 1 : 0), base = x * q + min(x, r);
-  const int P = (G - x + 7) / 8;
-  bool first = true;
-  for (int rd = 0; rd * P < n_x; ++rd) {
-    const int i = rd * P + ((rd & 1) ? P - 1 - k : k);
-    if (i >= n_x) continue;
-    if (!first) __syncthreads();
-    first = false;
-    fa16_item<GRP_B>(a, base + i, (rd & 1) != 0, smem_addr);
-  }
-}
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa16_bf16_kernel(FaArgs a, int n_work) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[F16_LDS];
-  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-  if (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) >= 4)
-    fa16_rounds<true>(a, n_work, smem_addr);
-  else
-    fa16_rounds<false>(a, n_work, smem_addr);
-}
-
 // Rows [0, kv_end) of every sequence from the paged cache into a contiguous
 // [B * kv_end, row] buffer (one 16-byte chunk per thread); a block-table entry
 // outside the pool gives zeros and sets err_flags.
@@ -995,7 +652,7 @@ hipError_t launch_fa_bf16(const FaArgs& a, hipStream_t st) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(n, std::max(cus, 8));  // one workgroup per CU
-  hipLaunchKernelGGL(fa16_bf16_kernel, dim3((unsigned)grid), dim3(512), 0, st, a, (int)n);
+  hipLaunchKernelGGL(fa_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, (int)n);
   return hipGetLastError();
 }
 
